@@ -1,0 +1,228 @@
+"""CPU oracle for the quantized-communication codec (ctypes over numpy).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  The GPU library neither imports nor links it, and the two share
+no source.
+
+The arithmetic lives in ``qc_oracle.c`` (plain single-threaded C, fp32,
+no FMA contraction); this module only builds it with gcc and marshals numpy
+arrays.  Every function returns fresh numpy arrays; ``ef`` arrays are updated
+in place, exactly as the C functions do.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "qc_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+UNIFORM, FP8_ROWWISE, QSGD, SIGN = 0, 1, 2, 3
+
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (always when ``force``)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        stale = os.path.exists(LIB) and any(
+            os.path.getmtime(s) > os.path.getmtime(LIB)
+            for s in (SRC, os.path.join(HERE, "qc_oracle.h")))
+        if stale or not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P, I64, I32, U64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64
+        L.qco_payload_bytes.argtypes = [I32, I64, I32]
+        L.qco_payload_bytes.restype = I64
+        L.qco_philox4x32_10.argtypes = [P, P, P]
+        L.qco_e4m3_from_f32.argtypes = [ctypes.c_float]
+        L.qco_e4m3_from_f32.restype = ctypes.c_uint8
+        L.qco_e4m3_from_f32_n.argtypes = [P, I64, P]
+        L.qco_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.qco_e4m3_to_f32.restype = ctypes.c_float
+        L.qco_tree_sum.argtypes = [P, I64, I64]
+        L.qco_tree_sum.restype = ctypes.c_float
+        L.qco_encode_uniform.argtypes = [P, P, I64, I32, I32, P, P, P]
+        L.qco_decode_uniform.argtypes = [P, P, P, I64, I32, I32, P]
+        L.qco_encode_fp8_rowwise.argtypes = [P, I64, I32, P, P]
+        L.qco_decode_fp8_rowwise.argtypes = [P, P, I64, I32, P]
+        L.qco_encode_qsgd.argtypes = [P, P, I64, I32, U64, U64, P, P]
+        L.qco_decode_qsgd.argtypes = [P, P, I64, I32, P]
+        L.qco_encode_sign.argtypes = [P, I32, P, I64, I32, P, P]
+        L.qco_decode_sign.argtypes = [P, P, I64, I32, P]
+        L.qco_decode_one.argtypes = [I32, P, P, P, I64, I32, I32]
+        L.qco_decode_one.restype = ctypes.c_float
+        L.qco_dequant_accumulate.argtypes = [I32, P, P, P, I32, I64, I32, I32, P, I32]
+        L.qco_majority_vote.argtypes = [P, I32, I64, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _ef(ef):
+    if ef is None:
+        return None
+    if ef.dtype != np.float32 or not ef.flags.c_contiguous:
+        raise TypeError("ef must be a contiguous float32 array (updated in place)")
+    return ef
+
+
+def nbuckets(n: int, group: int) -> int:
+    return -(-n // group)
+
+
+def payload_bytes(fmt: int, n: int, bits: int = 8) -> int:
+    return int(lib().qco_payload_bytes(fmt, n, bits))
+
+
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().qco_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def e4m3_from_f32(y: float) -> int:
+    return int(lib().qco_e4m3_from_f32(ctypes.c_float(y)))
+
+
+def e4m3_from_f32_n(y) -> np.ndarray:
+    """Codes of an array (each value clamped to [-448, 448] first)."""
+    y = _f32(y)
+    out = np.empty(y.size, dtype=np.uint8)
+    lib().qco_e4m3_from_f32_n(_p(y), y.size, _p(out))
+    return out
+
+
+def e4m3_to_f32(c: int) -> float:
+    return float(np.float32(lib().qco_e4m3_to_f32(c)))
+
+
+def tree_sum(terms, pow2len: int) -> np.float32:
+    t = _f32(terms)
+    return np.float32(lib().qco_tree_sum(_p(t), t.size, pow2len))
+
+
+def encode_uniform(x, ef, bucket: int, bits: int):
+    x = _f32(x)
+    ef = _ef(ef)
+    n = x.size
+    nb = nbuckets(n, bucket)
+    payload = np.empty(payload_bytes(UNIFORM, n, bits), dtype=np.uint8)
+    scale = np.empty(nb, dtype=np.float32)
+    zero = np.empty(nb, dtype=np.float32)
+    lib().qco_encode_uniform(_p(x), _p(ef), n, bucket, bits, _p(payload), _p(scale), _p(zero))
+    return payload, scale, zero
+
+
+def decode_uniform(payload, scale, zero, n: int, bucket: int, bits: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_uniform(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(scale)),
+                             _p(_f32(zero)), n, bucket, bits, _p(out))
+    return out
+
+
+def encode_fp8_rowwise(x, rows: int, dim: int):
+    x = _f32(x)
+    assert x.size == rows * dim
+    payload = np.empty(payload_bytes(FP8_ROWWISE, rows * dim), dtype=np.uint8)
+    scale = np.empty(rows, dtype=np.float32)
+    lib().qco_encode_fp8_rowwise(_p(x), rows, dim, _p(payload), _p(scale))
+    return payload, scale
+
+
+def decode_fp8_rowwise(payload, scale, rows: int, dim: int):
+    out = np.empty(rows * dim, dtype=np.float32)
+    lib().qco_decode_fp8_rowwise(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(scale)),
+                                 rows, dim, _p(out))
+    return out
+
+
+def encode_qsgd(x, ef, bucket: int, seed: int, elem_offset: int = 0):
+    x = _f32(x)
+    ef = _ef(ef)
+    n = x.size
+    if elem_offset % 4:
+        raise ValueError("elem_offset must be a multiple of 4")
+    payload = np.empty(payload_bytes(QSGD, n, 4), dtype=np.uint8)
+    norm = np.empty(nbuckets(n, bucket), dtype=np.float32)
+    lib().qco_encode_qsgd(_p(x), _p(ef), n, bucket, seed & (2**64 - 1), elem_offset,
+                          _p(payload), _p(norm))
+    return payload, norm
+
+
+def decode_qsgd(payload, norm, n: int, bucket: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_qsgd(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(norm)), n, bucket,
+                          _p(out))
+    return out
+
+
+def encode_sign(x, ef, bucket: int):
+    """x: float32 array, or uint16 array of bf16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        is_bf16 = 1
+    elif x.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("x must be float32 or uint16 (bf16 bits)")
+    ef = _ef(ef)
+    n = x.size
+    payload = np.empty(payload_bytes(SIGN, n, 1), dtype=np.uint8)
+    scale = np.empty(nbuckets(n, bucket), dtype=np.float32)
+    lib().qco_encode_sign(_p(x), is_bf16, _p(ef), n, bucket, _p(payload), _p(scale))
+    return payload, scale
+
+
+def decode_sign(payload, scale, n: int, bucket: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_sign(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(scale)), n, bucket,
+                          _p(out))
+    return out
+
+
+def dequant_accumulate(fmt: int, payloads, scale, zero, m: int, n: int, group: int, bits: int,
+                       acc=None):
+    """payloads: uint8 [m * payload_bytes]; scale/zero: float32 [m * nb].
+    If ``acc`` is given it is the starting value (accumulate=1) and is not
+    modified; the result is returned as a new array."""
+    payloads = np.ascontiguousarray(payloads, np.uint8)
+    out = np.zeros(n, dtype=np.float32) if acc is None else _f32(acc).copy()
+    z = None if zero is None else _f32(zero)
+    lib().qco_dequant_accumulate(fmt, _p(payloads), _p(_f32(scale)), _p(z), m, n, group, bits,
+                                 _p(out), 0 if acc is None else 1)
+    return out
+
+
+def majority_vote(payloads, m: int, n: int):
+    payloads = np.ascontiguousarray(payloads, np.uint8)
+    out = np.empty(payload_bytes(SIGN, n, 1), dtype=np.uint8)
+    lib().qco_majority_vote(_p(payloads), m, n, _p(out))
+    return out
