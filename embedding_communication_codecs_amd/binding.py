@@ -1,0 +1,184 @@
+"""ctypes binding of libqc with the C ABI's names (see include/qc.h).
+
+Argument marshalling only: every codec step runs in the HIP kernels behind
+the C ABI.  Array arguments may be torch tensors (their device pointer is
+passed) or plain integers (raw device addresses, passed unchecked).  For
+tensors the binding also checks that each buffer is on the GPU, contiguous
+and large enough for what the call will read or write, so a size mistake is
+a Python exception instead of an out-of-bounds access.  A non-zero status
+from the library raises QcError.  There is no CPU fallback: if libqc.so has
+not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqc.so")
+
+QC_OK, QC_ERR_ARG, QC_ERR_ALIGN, QC_ERR_UNSUPPORTED, QC_ERR_LAUNCH = 0, 1, 2, 3, 4
+QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN = 0, 1, 2, 3
+QC_F32, QC_BF16 = 0, 1
+QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
+
+EXPORTS = (
+    "qc_encode_uniform", "qc_encode_fp8_rowwise", "qc_encode_qsgd", "qc_encode_sign",
+    "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
+)
+
+
+class QcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m embedding_communication_codecs_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        sig = {
+            "qc_encode_uniform": [P, P, I64, I32, I32, P, P, P, P],
+            "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
+            "qc_encode_qsgd": [P, P, I64, I32, I32, U64, U64, P, P, P],
+            "qc_encode_sign": [P, I32, P, I64, I32, P, P, P],
+            "qc_decode": [I32, P, P, P, I64, I32, I32, P, P],
+            "qc_dequant_accumulate": [I32, P, P, P, I32, I64, I32, I32, P, I32, P, P, P, P],
+            "qc_majority_vote": [P, I32, I64, P, P],
+            "qc_payload_bytes": [I32, I64, I32, I32],
+            "qc_status_str": [I32],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.qc_payload_bytes.restype = I64
+        L.qc_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------- helpers
+
+
+def payload_bytes(fmt: int, n: int, group: int = 64, bits: int = 8) -> int:
+    return int(lib().qc_payload_bytes(fmt, n, group, bits))
+
+
+def nbuckets(n: int, group: int) -> int:
+    return -(-n // group)
+
+
+def _bytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _ptr(t, need_bytes: int | None, name: str):
+    """Device address of a tensor/int/None, checking capacity for tensors."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if need_bytes is not None and _bytes(t) < need_bytes:
+        raise ValueError(f"{name} holds {_bytes(t)} bytes, the call needs {need_bytes}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != QC_OK:
+        raise QcError(status, lib().qc_status_str(status).decode())
+
+
+# ------------------------------------------------------------ entry points
+
+
+def qc_encode_uniform(x, ef, n, bucket, bits, codes, scale, zero, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in (4, 8) and n >= 0 else None
+    _check(lib().qc_encode_uniform(
+        _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, bits, _ptr(codes, pb, "codes"),
+        _ptr(scale, 4 * nb, "scale"), _ptr(zero, 4 * nb, "zero"), _stream(stream)))
+
+
+def qc_encode_fp8_rowwise(x, rows, dim, codes, scale, stream=None):
+    n = rows * dim
+    pb = payload_bytes(QC_FP8_ROWWISE, n, dim, 8) if n >= 0 else None
+    _check(lib().qc_encode_fp8_rowwise(
+        _ptr(x, 4 * n, "x"), rows, dim, _ptr(codes, pb, "codes"), _ptr(scale, 4 * max(rows, 0), "scale"),
+        _stream(stream)))
+
+
+def qc_encode_qsgd(x, ef, n, bucket, levels, seed, elem_offset, words, norm, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_QSGD, n, bucket, 16) if n >= 0 else None
+    _check(lib().qc_encode_qsgd(
+        _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, levels, seed & (2**64 - 1),
+        elem_offset, _ptr(words, pb, "words"), _ptr(norm, 4 * nb, "norm"), _stream(stream)))
+
+
+def qc_encode_sign(x, xtype, ef, n, bucket, words, scale, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_SIGN, n, bucket, 1) if n >= 0 else None
+    xbytes = (2 if xtype == QC_BF16 else 4) * n
+    _check(lib().qc_encode_sign(
+        _ptr(x, xbytes, "x"), xtype, _ptr(ef, 4 * n, "ef"), n, bucket, _ptr(words, pb, "words"),
+        _ptr(scale, 4 * nb, "scale"), _stream(stream)))
+
+
+def qc_decode(fmt, codes, scale, zero, n, group, bits, out, stream=None):
+    nb = nbuckets(n, group) if n > 0 and group > 0 else 0
+    pb = payload_bytes(fmt, n, group, bits) if n >= 0 else -1
+    _check(lib().qc_decode(
+        fmt, _ptr(codes, pb if pb >= 0 else None, "codes"), _ptr(scale, 4 * nb, "scale"),
+        _ptr(zero, 4 * nb, "zero"), n, group, bits, _ptr(out, 4 * n, "out"), _stream(stream)))
+
+
+def qc_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, acc, accumulate,
+                          rq_codes=None, rq_scale=None, rq_zero=None, stream=None):
+    nb = nbuckets(n, group) if n > 0 and group > 0 else 0
+    pb = payload_bytes(fmt, n, group, bits) if n >= 0 else -1
+    mm = max(m, 0)
+    rq_pb = payload_bytes(QC_UNIFORM, n, group, bits) if bits in (4, 8) and n >= 0 else None
+    _check(lib().qc_dequant_accumulate(
+        fmt, _ptr(codes, mm * pb if pb >= 0 else None, "codes"), _ptr(scale, 4 * mm * nb, "scale"),
+        _ptr(zero, 4 * mm * nb, "zero"), m, n, group, bits, _ptr(acc, 4 * n, "acc"),
+        1 if accumulate else 0, _ptr(rq_codes, rq_pb, "rq_codes"), _ptr(rq_scale, 4 * nb, "rq_scale"),
+        _ptr(rq_zero, 4 * nb, "rq_zero"), _stream(stream)))
+
+
+def qc_majority_vote(words, m, n, out_words, stream=None):
+    pb = payload_bytes(QC_SIGN, n, 64, 1) if n >= 0 else None
+    _check(lib().qc_majority_vote(
+        _ptr(words, max(m, 0) * pb if pb is not None else None, "words"), m, n,
+        _ptr(out_words, pb, "out_words"), _stream(stream)))
+
+
+def qc_payload_bytes(fmt, n, group, bits) -> int:
+    return int(lib().qc_payload_bytes(fmt, n, group, bits))
+
+
+def qc_status_str(status) -> str:
+    return lib().qc_status_str(status).decode()

@@ -1,0 +1,313 @@
+// k_accumulate.hip -- receive side: acc = (acc or +0) + DQ_0 + ... + DQ_{m-1}
+// over m payloads resident in HBM, optionally requantized to uniform codes
+// in the same pass.
+//
+// Each lane owns 16 consecutive elements per chunk (one 16-byte load of
+// INT8/FP8 codes per worker, 8 bytes for 4-bit, 2 bytes for sign) and keeps
+// their fp32 sums in registers while it walks the workers in order, so the
+// result is bit-identical to adding the decoded terms one worker at a time.
+// Loads for UW workers are issued before their terms are added.  A bucket
+// (group) is held by LPB lanes x K chunks x W waves (the layout of
+// qc_bucket.hpp with E = 16), which is what the fused requantization needs
+// to reduce min/max over the bucket without a second pass over acc.
+//
+// The per-(worker, bucket) scale and zero are uniform across a wave when a
+// bucket spans whole waves, and are then read through the scalar cache.
+// Blocks are mapped to buckets XCD by XCD (consecutive buckets on one XCD),
+// so neighbouring buckets' statistics share that XCD's L2 lines.
+//
+// Bounds: a chunk starting below n reads its codes inside the 16-byte
+// padded payload (see the payload rules in qc.h).
+#include "qc_device.hpp"
+#include "qc_bucket.hpp"
+#include "qc_launch.hpp"
+
+namespace qc {
+namespace {
+
+enum { A_U8 = 0, A_U4 = 1, A_FP8 = 2, A_QSGD = 3, A_SIGN = 4 };
+
+// Raw code bits of a 16-element chunk starting at element i of a payload.
+template <int F>
+struct ChunkBits {
+    u32x4 v;
+};
+
+template <int F>
+__device__ __forceinline__ ChunkBits<F> load_chunk(const uint8_t* __restrict__ p, int64_t i) {
+    ChunkBits<F> r;
+    if constexpr (F == A_U8 || F == A_FP8) {
+        r.v = ld_u4(p + i);
+    } else if constexpr (F == A_U4 || F == A_QSGD) {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(p + i / 2);
+        r.v = u32x4{h.x, h.y, 0u, 0u};
+    } else {
+        const uint32_t h = *reinterpret_cast<const uint16_t*>(p + i / 8);
+        r.v = u32x4{h, 0u, 0u, 0u};
+    }
+    return r;
+}
+
+// Decoded value of element j (0..15) of a chunk.  For QSGD `z` is d.
+template <int F>
+__device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s, float z) {
+    const uint32_t words[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
+    if constexpr (F == A_U8) {
+        const float p = (float)((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
+        return p + z;
+    } else if constexpr (F == A_FP8) {
+        return e4m3_decode((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
+    } else if constexpr (F == A_U4) {
+        const float p = (float)((words[j >> 3] >> (4 * (j & 7))) & 0xFu) * s;
+        return p + z;
+    } else if constexpr (F == A_QSGD) {
+        const uint32_t code = (words[j >> 3] >> (4 * (j & 7))) & 0xFu;
+        const uint32_t level = code & 7u;
+        const float mag = (float)level * z;
+        return level == 0u ? 0.0f : ((code & 8u) ? -mag : mag);
+    } else {
+        return ((words[0] >> j) & 1u) ? -s : s;
+    }
+}
+
+template <class G, int F, int RQBITS, bool RQ>
+__global__ void __launch_bounds__(G::THREADS)
+k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+              const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb, int64_t pbytes,
+              float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,
+              int64_t rq_pbytes, float* __restrict__ rq_scale, float* __restrict__ rq_zero) {
+    constexpr int K = G::K, LPB = G::LPB, UW = 4;
+    __shared__ float lds[G::W];
+
+    // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs,
+    // so block b runs on XCD b%8; give each XCD a contiguous bucket range.
+    const int64_t nblk = gridDim.x;
+    const int64_t per_xcd = (nblk + 7) / 8;
+    const int64_t vblock = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (vblock * G::BPB >= nb) return;  // spare blocks when gridDim.x % 8 != 0
+
+    const int64_t first = G::W > 1 ? vblock
+                                   : vblock * G::BPB + wave_id() * G::GROUPS + lane_id() / LPB;
+    for (int64_t bk = first; bk < nb; bk += (int64_t)per_xcd * 8 * G::BPB) {
+        int64_t bks = bk;
+        if constexpr (LPB == WAVE) bks = __builtin_amdgcn_readfirstlane((int)bk);
+        const int64_t base = bks * (int64_t)G::B + lane_offset<G>();
+
+        float a[K][16];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t i = base + (int64_t)k * LPB * 16;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) a[k][j] = 0.0f;
+            if (accumulate) {
+                if (i + 16 <= n) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 t = ld_f4(acc + i + 4 * q);
+                        a[k][4 * q] = t.x; a[k][4 * q + 1] = t.y;
+                        a[k][4 * q + 2] = t.z; a[k][4 * q + 3] = t.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (i + j < n) a[k][j] = acc[i + j];
+                }
+            }
+        }
+
+        int32_t w0 = 0;
+        for (; w0 + UW <= m; w0 += UW) {
+            ChunkBits<F> c[UW][K];
+            float s[UW], z[UW];
+#pragma unroll
+            for (int u = 0; u < UW; ++u) {
+                const uint8_t* pw = codes + (int64_t)(w0 + u) * pbytes;
+                s[u] = scale[(int64_t)(w0 + u) * nb + bks];
+                if constexpr (F == A_U8 || F == A_U4) z[u] = zero[(int64_t)(w0 + u) * nb + bks];
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int64_t i = base + (int64_t)k * LPB * 16;
+                    c[u][k] = i < n ? load_chunk<F>(pw, i) : ChunkBits<F>{u32x4{0u, 0u, 0u, 0u}};
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UW; ++u) {
+                if constexpr (F == A_QSGD) z[u] = s[u] / 7.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(c[u][k], j, s[u], z[u]);
+            }
+        }
+        for (; w0 < m; ++w0) {
+            const uint8_t* pw = codes + (int64_t)w0 * pbytes;
+            const float s = scale[(int64_t)w0 * nb + bks];
+            float z = 0.0f;
+            if constexpr (F == A_U8 || F == A_U4) z = zero[(int64_t)w0 * nb + bks];
+            if constexpr (F == A_QSGD) z = s / 7.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int64_t i = base + (int64_t)k * LPB * 16;
+                const ChunkBits<F> c = i < n ? load_chunk<F>(pw, i) : ChunkBits<F>{u32x4{0u, 0u, 0u, 0u}};
+#pragma unroll
+                for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(c, j, s, z);
+            }
+        }
+
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t i = base + (int64_t)k * LPB * 16;
+            if (i + 16 <= n) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    st_f4(acc + i + 4 * q, f32x4{a[k][4 * q], a[k][4 * q + 1], a[k][4 * q + 2], a[k][4 * q + 3]});
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (i + j < n) acc[i + j] = a[k][j];
+            }
+        }
+
+        if constexpr (RQ) {
+            // requantize the bucket's sums: the uniform rule with no feedback
+            constexpr uint32_t L = (1u << RQBITS) - 1u;
+            float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (base + (int64_t)k * LPB * 16 + j < n) {
+                        mn = fminf(mn, a[k][j]);
+                        mx = fmaxf(mx, a[k][j]);
+                    }
+            mn = group_min<LPB>(mn);
+            mx = group_max<LPB>(mx);
+            if constexpr (G::W > 1) {
+                mn = block_min<G::W>(mn, lds);
+                mx = block_max<G::W>(mx, lds);
+            }
+            mn = mn + 0.0f;
+            mx = mx + 0.0f;
+            const float sc = (mx - mn) / (float)L;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int64_t i = base + (int64_t)k * LPB * 16;
+                uint32_t q[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    uint32_t cq = 0;
+                    if (sc != 0.0f) {
+                        const float t = (a[k][j] - mn) / sc;
+                        cq = (uint32_t)fminf(fmaxf(__builtin_rintf(t), 0.0f), (float)L);
+                    }
+                    q[j] = (i + j < n) ? cq : 0u;
+                }
+                if constexpr (RQBITS == 8) {
+                    u32x4 o;
+                    o.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+                    o.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+                    o.z = q[8] | (q[9] << 8) | (q[10] << 16) | (q[11] << 24);
+                    o.w = q[12] | (q[13] << 8) | (q[14] << 16) | (q[15] << 24);
+                    if (i < rq_pbytes) st_u4(rq_codes + i, o);
+                } else {
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        lo |= q[j] << (4 * j);
+                        hi |= q[8 + j] << (4 * j);
+                    }
+                    if (i / 2 < rq_pbytes) {
+                        st_u32(rq_codes + i / 2, lo);
+                        st_u32(rq_codes + i / 2 + 4, hi);
+                    }
+                }
+            }
+            if (bucket_leader<G>()) {
+                rq_scale[bk] = sc;
+                rq_zero[bk] = mn;
+            }
+        }
+    }
+}
+
+// Bucket of `group` elements as LPB lanes x K chunks of 16 x W waves: whole
+// waves with up to 4 chunks per lane before spreading over more waves.
+template <class Fn>
+hipError_t dispatch_group(int32_t group, Fn&& fn) {
+    switch (group / 16) {
+        case 4: return fn(Geom<16, 4, 1, 1>{});
+        case 8: return fn(Geom<16, 8, 1, 1>{});
+        case 16: return fn(Geom<16, 16, 1, 1>{});
+        case 32: return fn(Geom<16, 32, 1, 1>{});
+        case 64: return fn(Geom<16, 64, 1, 1>{});
+        case 128: return fn(Geom<16, 64, 2, 1>{});
+        case 256: return fn(Geom<16, 64, 4, 1>{});
+        case 512: return fn(Geom<16, 64, 4, 2>{});
+        case 1024: return fn(Geom<16, 64, 4, 4>{});
+        case 2048: return fn(Geom<16, 64, 4, 8>{});
+        case 4096: return fn(Geom<16, 64, 4, 16>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int F>
+hipError_t launch_fmt(const void* codes, const float* scale, const float* zero, int32_t m, int64_t n,
+                      int32_t group, int32_t bits, int64_t pbytes, float* acc, bool accumulate,
+                      void* rq_codes, float* rq_scale, float* rq_zero, hipStream_t stream) {
+    const int64_t nb = (n + group - 1) / group;
+    return dispatch_group(group, [&](auto g) {
+        using G = decltype(g);
+        int64_t blocks = grid_for(nb, G::BPB);
+        blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+        const dim3 grid((unsigned)blocks), block(G::THREADS);
+        const int64_t rq_pbytes = bits == 8 ? (n + 15) / 16 * 16 : ((n + 7) / 8 * 4 + 15) / 16 * 16;
+        if (rq_codes == nullptr) {
+            hipLaunchKernelGGL((k_dequant_acc<G, F, 8, false>), grid, block, 0, stream,
+                               (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                               (int32_t)accumulate, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr,
+                               (float*)nullptr);
+        } else if constexpr (F == A_U8 || F == A_U4) {
+            if (bits == 8)
+                hipLaunchKernelGGL((k_dequant_acc<G, F, 8, true>), grid, block, 0, stream,
+                                   (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                                   (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale,
+                                   rq_zero);
+            else
+                hipLaunchKernelGGL((k_dequant_acc<G, F, 4, true>), grid, block, 0, stream,
+                                   (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                                   (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale,
+                                   rq_zero);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    });
+}
+
+}  // namespace
+
+hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float* scale,
+                                     const float* zero, int32_t m, int64_t n, int32_t group,
+                                     int32_t bits, int64_t payload_bytes, float* acc,
+                                     bool accumulate, void* rq_codes, float* rq_scale,
+                                     float* rq_zero, hipStream_t stream) {
+    switch (fmt) {
+        case 0:
+            if (bits == 8)
+                return launch_fmt<A_U8>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                        accumulate, rq_codes, rq_scale, rq_zero, stream);
+            return launch_fmt<A_U4>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                    accumulate, rq_codes, rq_scale, rq_zero, stream);
+        case 1:
+            return launch_fmt<A_FP8>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                     accumulate, rq_codes, rq_scale, rq_zero, stream);
+        case 2:
+            return launch_fmt<A_QSGD>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                      accumulate, rq_codes, rq_scale, rq_zero, stream);
+        default:
+            return launch_fmt<A_SIGN>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                      accumulate, rq_codes, rq_scale, rq_zero, stream);
+    }
+}
+
+}  // namespace qc

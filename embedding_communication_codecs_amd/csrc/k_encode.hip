@@ -1,0 +1,409 @@
+// k_encode.hip -- gradient encoders with fused error feedback:
+//   uniform INT8/INT4, QSGD (Philox stochastic rounding, 4-bit), 1-bit sign.
+//
+// Every encoder makes one HBM pass: a lane group loads its bucket into
+// registers (v = ef + x), reduces the bucket statistic across lanes, then
+// quantizes, packs and writes codes and the new residual from registers.
+#include "qc_device.hpp"
+#include "qc_bucket.hpp"
+#include "qc_launch.hpp"
+
+namespace qc {
+namespace {
+
+// --------------------------------------------------------------- loading
+// Load chunk k (E = 4 fp32 elements at index i) as v = ef + x.  Elements at
+// or past n read as 0 and are masked by the caller.
+template <bool FULL>
+__device__ __forceinline__ void load4(const float* __restrict__ x, const float* __restrict__ ef,
+                                      int64_t i, int64_t n, float (&v)[4]) {
+    if (FULL || i + 4 <= n) {
+        f32x4 g = ld_f4(x + i);
+        if (ef) g = ld_f4(ef + i) + g;
+        v[0] = g.x; v[1] = g.y; v[2] = g.z; v[3] = g.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float g = 0.0f;
+            if (i + j < n) {
+                g = x[i + j];
+                if (ef) g = ef[i + j] + g;
+            }
+            v[j] = g;
+        }
+    }
+}
+
+template <bool FULL>
+__device__ __forceinline__ void store_ef4(float* __restrict__ ef, int64_t i, int64_t n,
+                                          const float (&e)[4]) {
+    if (FULL || i + 4 <= n) {
+        st_f4(ef + i, f32x4{e[0], e[1], e[2], e[3]});
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j < n) ef[i + j] = e[j];
+    }
+}
+
+// ============================================================== uniform
+// scale = (max - min) / (2^BITS - 1); code = rint((v - min) / scale);
+// DQ = code*scale + min; ef = v - DQ.
+
+template <class G, int BITS, bool FULL>
+__device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, float* __restrict__ ef,
+                                               int64_t n, int64_t bk, uint8_t* __restrict__ codes,
+                                               int64_t pbytes, float* __restrict__ scale,
+                                               float* __restrict__ zero, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB;
+    constexpr uint32_t L = (1u << BITS) - 1u;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+
+    float v[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) load4<FULL>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (FULL || base + (int64_t)k * LPB * 4 + j < n) {
+                mn = fminf(mn, v[k][j]);
+                mx = fmaxf(mx, v[k][j]);
+            }
+    mn = group_min<LPB>(mn);
+    mx = group_max<LPB>(mx);
+    if constexpr (G::W > 1) {
+        mn = block_min<G::W>(mn, lds);
+        mx = block_max<G::W>(mx, lds);
+    }
+    mn = mn + 0.0f;  // a -0 extreme becomes +0
+    mx = mx + 0.0f;
+    const float sc = (mx - mn) / (float)L;
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 4;
+        uint32_t q[4];
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t c = 0;
+            if (sc != 0.0f) {
+                const float t = (v[k][j] - mn) / sc;
+                const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), (float)L);
+                c = (uint32_t)r;
+            }
+            if (!FULL && i + j >= n) c = 0;
+            q[j] = c;
+            const float p = (float)c * sc;
+            const float dq = p + mn;
+            e[j] = v[k][j] - dq;
+        }
+        if constexpr (BITS == 8) {
+            const uint32_t word = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            if (i < pbytes) st_u32(codes + i, word);
+        } else {
+            const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
+            const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
+            if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(codes + i / 2, half | (other << 16));
+        }
+        if (ef) store_ef4<FULL>(ef, i, n, e);
+    }
+    if (bucket_leader<G>()) {
+        scale[bk] = sc;
+        zero[bk] = mn;
+    }
+}
+
+template <class G, int BITS>
+__global__ void __launch_bounds__(G::THREADS)
+k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
+              uint8_t* __restrict__ codes, int64_t pbytes, float* __restrict__ scale,
+              float* __restrict__ zero) {
+    __shared__ float lds[G::W];
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        if ((bk + 1) * (int64_t)G::B <= n)
+            uniform_bucket<G, BITS, true>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+        else
+            uniform_bucket<G, BITS, false>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+    }
+}
+
+// ================================================================= QSGD
+// norm = sqrt(pairwise sum of v^2); d = norm/7; level = floor(|v|/d) + Bernoulli(frac)
+// drawn from Philox4x32-10 word g%4 of counter g/4 (g = global index).
+
+template <class G, bool FULL>
+__device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* __restrict__ ef,
+                                            int64_t n, int64_t bk, uint32_t k0, uint32_t k1,
+                                            uint64_t elem_offset, uint8_t* __restrict__ words,
+                                            int64_t pbytes, float* __restrict__ norm, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+
+    float v[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) load4<FULL>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+
+    float s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const float a0 = v[k][0] * v[k][0], a1 = v[k][1] * v[k][1];
+        const float a2 = v[k][2] * v[k][2], a3 = v[k][3] * v[k][3];
+        s[k] = group_sum<LPB>((a0 + a1) + (a2 + a3));
+    }
+    float ss = tree_sum_regs<K>(s);
+    if constexpr (G::W > 1) ss = block_tree_sum<G::W>(ss, lds);
+    const float nrm = sqrtf(ss);
+    const float d = nrm / 7.0f;
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 4;
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+        float e[4] = {v[k][0], v[k][1], v[k][2], v[k][3]};
+        if (d != 0.0f && (FULL || i < n)) {
+            const uint64_t blk = (elem_offset + (uint64_t)i) >> 2;
+            const u32x4 r = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u, k0, k1);
+            const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = fabsf(v[k][j]) / d;
+                const float fl = floorf(t);
+                const float frac = t - fl;
+                const float u = (float)(rw[j] >> 8) * 0x1p-24f;
+                uint32_t level = (uint32_t)fl + (u < frac ? 1u : 0u);
+                level = level < 7u ? level : 7u;
+                if (!FULL && i + j >= n) level = 0;
+                if (level != 0u) {
+                    const bool neg = v[k][j] < 0.0f;
+                    q[j] = (neg ? 8u : 0u) | level;
+                    const float mag = (float)level * d;
+                    e[j] = v[k][j] - (neg ? -mag : mag);
+                }
+            }
+        }
+        const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
+        const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
+        if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(words + i / 2, half | (other << 16));
+        if (ef) store_ef4<FULL>(ef, i, n, e);
+    }
+    if (bucket_leader<G>()) norm[bk] = nrm;
+}
+
+template <class G>
+__global__ void __launch_bounds__(G::THREADS)
+k_enc_qsgd(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0,
+           uint32_t k1, uint64_t elem_offset, uint8_t* __restrict__ words, int64_t pbytes,
+           float* __restrict__ norm) {
+    __shared__ float lds[G::W];
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        if ((bk + 1) * (int64_t)G::B <= n)
+            qsgd_bucket<G, true>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
+        else
+            qsgd_bucket<G, false>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
+    }
+}
+
+// ================================================================= sign
+// scale = (pairwise sum of |v|) / count; bit = v < 0; DQ = bit ? -scale : scale.
+// fp32 input: chunks of 4 elements; bf16 input: chunks of 8 (16 bytes).
+
+template <class G, bool BF16, bool FULL>
+__device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* __restrict__ ef,
+                                            int64_t n, int64_t bk, int64_t nb,
+                                            uint8_t* __restrict__ words, int64_t pbytes,
+                                            float* __restrict__ scale, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB, E = G::E;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+
+    float v[K][E];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * E;
+        if constexpr (BF16) {
+            const uint16_t* x = static_cast<const uint16_t*>(xv);
+            if (FULL || i + E <= n) {
+                const u32x4 w = ld_u4(x + i);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[k][2 * h] = bf16_to_f32(ww[h] & 0xFFFFu);
+                    v[k][2 * h + 1] = bf16_to_f32(ww[h] >> 16);
+                }
+                if (ef) {
+                    const f32x4 e0 = ld_f4(ef + i), e1 = ld_f4(ef + i + 4);
+                    const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[k][j] = ee[j] + v[k][j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    float g = 0.0f;
+                    if (i + j < n) {
+                        g = bf16_to_f32(x[i + j]);
+                        if (ef) g = ef[i + j] + g;
+                    }
+                    v[k][j] = g;
+                }
+            }
+        } else {
+            const float* x = static_cast<const float*>(xv);
+            float t[4];
+            load4<FULL>(x, ef, i, n, t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[k][j] = t[j];
+        }
+    }
+
+    // sum of |v|: chunk-local pairwise tree, then lanes, chunks and waves
+    float s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float a[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) a[j] = fabsf(v[k][j]);  // masked elements are +0
+        s[k] = group_sum<LPB>(tree_sum_regs<E>(a));
+    }
+    float S = tree_sum_regs<K>(s);
+    if constexpr (G::W > 1) S = block_tree_sum<G::W>(S, lds);
+    const int64_t cnt = FULL ? (int64_t)G::B : n - bk * (int64_t)G::B;
+    const float sc = S / (float)cnt;
+
+    constexpr int LPW = 32 / E;  // lanes per 32-bit output word
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * E;
+        uint32_t bits = 0;
+        float e[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const bool neg = v[k][j] < 0.0f;
+            bits |= (neg ? 1u : 0u) << j;
+            e[j] = v[k][j] - (neg ? -sc : sc);
+        }
+        const uint32_t word = group_or<LPW>(bits << (E * (lane_id() % LPW)));
+        if (lane_id() % LPW == 0 && i / 8 < pbytes) st_u32(words + i / 8, word);
+        if (ef) {
+            if constexpr (E == 8) {
+                if (FULL || i + 8 <= n) {
+                    st_f4(ef + i, f32x4{e[0], e[1], e[2], e[3]});
+                    st_f4(ef + i + 4, f32x4{e[4], e[5], e[6], e[7]});
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (i + j < n) ef[i + j] = e[j];
+                }
+            } else {
+                float e4[4] = {e[0], e[1], e[2], e[3]};
+                store_ef4<FULL>(ef, i, n, e4);
+            }
+        }
+    }
+    if (bucket_leader<G>()) {
+        scale[bk] = sc;
+        // 64-element buckets span 8 bytes; the payload is padded to 16, so
+        // the last bucket also zeroes any padding words past its own end.
+        if (bk == nb - 1)
+            for (int64_t b = (bk + 1) * (int64_t)G::B / 8; b < pbytes; b += 4) st_u32(words + b, 0u);
+    }
+}
+
+template <class G, bool BF16>
+__global__ void __launch_bounds__(G::THREADS)
+k_enc_sign(const void* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
+           uint8_t* __restrict__ words, int64_t pbytes, float* __restrict__ scale) {
+    __shared__ float lds[G::W];
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        // masked elements load as +0: v < 0 is false, so their bits are 0
+        if ((bk + 1) * (int64_t)G::B <= n)
+            sign_bucket<G, BF16, true>(x, ef, n, bk, nb, words, pbytes, scale, lds);
+        else
+            sign_bucket<G, BF16, false>(x, ef, n, bk, nb, words, pbytes, scale, lds);
+    }
+}
+
+// ============================================================ dispatch
+// Geometry per bucket size: LPB lanes per bucket, K chunks per lane, W waves
+// per bucket.  A single wave holds up to K = 8 chunks per lane (32 or 64
+// values in registers); larger buckets spread over W waves of K = 8, and
+// K = 16 only where W would otherwise exceed 16 (1024 threads).
+
+template <int E, class F>
+hipError_t dispatch_bucket(int32_t bucket, F&& f) {
+    const int chunks = bucket / E;
+    switch (chunks) {
+        case 8: if constexpr (E == 8) return f(Geom<E, 8, 1, 1>{}); break;
+        case 16: return f(Geom<E, 16, 1, 1>{});
+        case 32: return f(Geom<E, 32, 1, 1>{});
+        case 64: return f(Geom<E, 64, 1, 1>{});
+        case 128: return f(Geom<E, 64, 2, 1>{});
+        case 256: return f(Geom<E, 64, 4, 1>{});
+        case 512: return f(Geom<E, 64, 8, 1>{});
+        case 1024: return f(Geom<E, 64, 8, 2>{});
+        case 2048: return f(Geom<E, 64, 8, 4>{});
+        case 4096: return f(Geom<E, 64, 8, 8>{});
+        case 8192: return f(Geom<E, 64, 8, 16>{});
+        case 16384: if constexpr (E == 4) return f(Geom<E, 64, 16, 16>{}); break;
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                                 void* codes, int64_t payload_bytes, float* scale, float* zero,
+                                 hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        if (bits == 8)
+            hipLaunchKernelGGL((k_enc_uniform<G, 8>), grid, block, 0, stream, x, ef, n, nb,
+                               (uint8_t*)codes, payload_bytes, scale, zero);
+        else
+            hipLaunchKernelGGL((k_enc_uniform<G, 4>), grid, block, 0, stream, x, ef, n, nb,
+                               (uint8_t*)codes, payload_bytes, scale, zero);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                              uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,
+                              float* norm, hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        hipLaunchKernelGGL((k_enc_qsgd<G>), grid, block, 0, stream, x, ef, n, nb, (uint32_t)seed,
+                           (uint32_t)(seed >> 32), elem_offset, (uint8_t*)words, payload_bytes, norm);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_encode_sign(const void* x, bool bf16, float* ef, int64_t n, int32_t bucket,
+                              uint32_t* words, int64_t payload_bytes, float* scale,
+                              hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    if (bf16)
+        return dispatch_bucket<8>(bucket, [&](auto g) {
+            using G = decltype(g);
+            const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+            hipLaunchKernelGGL((k_enc_sign<G, true>), grid, block, 0, stream, x, ef, n, nb,
+                               (uint8_t*)words, payload_bytes, scale);
+            return hipGetLastError();
+        });
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        hipLaunchKernelGGL((k_enc_sign<G, false>), grid, block, 0, stream, x, ef, n, nb,
+                           (uint8_t*)words, payload_bytes, scale);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace qc

@@ -1,0 +1,194 @@
+// qc_api.cpp -- the C ABI of libqc (declared in include/qc.h).
+//
+// Each entry point validates every argument on the host before touching
+// the HIP runtime, so a rejected call enqueues nothing and writes nothing,
+// and the validation can be exercised on a machine without a GPU.  Valid
+// calls hand over to the launchers in the kernel sources.
+#include "../../include/qc.h"
+
+#include <hip/hip_runtime.h>
+
+#include "qc_launch.hpp"
+
+namespace {
+
+using qc::log2_exact;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool bad_bucket(int32_t b) {
+    return b < QC_MIN_BUCKET || b > QC_MAX_BUCKET || (b & (b - 1)) != 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int launched(hipError_t e) { return e == hipSuccess ? QC_OK : QC_ERR_LAUNCH; }
+
+hipStream_t hs(qc_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Bucket indices are handled as 32-bit values inside some kernels.
+constexpr int64_t kMaxBuckets = (int64_t(1) << 31) - 1;
+
+}  // namespace
+
+extern "C" {
+
+int64_t qc_payload_bytes(int32_t fmt, int64_t n, int32_t group, int32_t bits) {
+    (void)group;
+    if (n < 0) return -1;
+    int64_t code_bytes;
+    switch (fmt) {
+        case QC_UNIFORM:
+            if (bits == 8) code_bytes = n;
+            else if (bits == 4) code_bytes = 4 * ceil_div(n, 8);
+            else return -1;
+            break;
+        case QC_FP8_ROWWISE: code_bytes = n; break;
+        case QC_QSGD: code_bytes = 4 * ceil_div(n, 8); break;
+        case QC_SIGN: code_bytes = 4 * ceil_div(n, 32); break;
+        default: return -1;
+    }
+    return ceil_div(code_bytes, 16) * 16;
+}
+
+const char* qc_status_str(int32_t status) {
+    switch (status) {
+        case QC_OK: return "QC_OK";
+        case QC_ERR_ARG: return "QC_ERR_ARG: invalid argument";
+        case QC_ERR_ALIGN: return "QC_ERR_ALIGN: pointer not 16-byte aligned";
+        case QC_ERR_UNSUPPORTED: return "QC_ERR_UNSUPPORTED: unsupported format or parameter";
+        case QC_ERR_LAUNCH: return "QC_ERR_LAUNCH: kernel launch failed";
+        default: return "unknown qc status";
+    }
+}
+
+int qc_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                      void* codes, float* scale, float* zero, qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (bits != 8 && bits != 4) return QC_ERR_UNSUPPORTED;
+    if (n == 0) return QC_OK;
+    if (!x || !codes || !scale || !zero) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(codes) || misaligned(scale) || misaligned(zero))
+        return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_uniform(x, ef, n, bucket, bits, codes,
+                                              qc_payload_bytes(QC_UNIFORM, n, bucket, bits), scale,
+                                              zero, hs(stream)));
+}
+
+int qc_encode_fp8_rowwise(const float* x, int64_t rows, int32_t dim, uint8_t* codes, float* scale,
+                          qc_stream_t stream) {
+    if (rows < 0) return QC_ERR_ARG;
+    if (dim < 4 || dim > QC_MAX_BUCKET || dim % 4 != 0) return QC_ERR_UNSUPPORTED;
+    if (rows == 0) return QC_OK;
+    if (!x || !codes || !scale) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(codes) || misaligned(scale)) return QC_ERR_ALIGN;
+    const int64_t n = rows * (int64_t)dim;
+    return launched(qc::launch_encode_fp8(x, rows, dim, codes,
+                                          qc_payload_bytes(QC_FP8_ROWWISE, n, dim, 8), scale,
+                                          hs(stream)));
+}
+
+int qc_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, int32_t levels,
+                   uint64_t seed, uint64_t elem_offset, uint32_t* words, float* norm,
+                   qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket) || (elem_offset & 3u) != 0) return QC_ERR_ARG;
+    if (levels != 16) return QC_ERR_UNSUPPORTED;
+    if (n == 0) return QC_OK;
+    if (!x || !words || !norm) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(words) || misaligned(norm)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_qsgd(x, ef, n, bucket, seed, elem_offset, words,
+                                           qc_payload_bytes(QC_QSGD, n, bucket, 16), norm,
+                                           hs(stream)));
+}
+
+int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t bucket,
+                   uint32_t* words, float* scale, qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket) || (xtype != QC_F32 && xtype != QC_BF16)) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!x || !words || !scale) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(words) || misaligned(scale)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_sign(x, xtype == QC_BF16, ef, n, bucket, words,
+                                           qc_payload_bytes(QC_SIGN, n, bucket, 1), scale,
+                                           hs(stream)));
+}
+
+namespace {
+
+// Format/bits/group checks shared by qc_decode and qc_dequant_accumulate.
+int check_format(int32_t fmt, int64_t n, int32_t group, int32_t bits, const float* zero,
+                 bool accumulate_path) {
+    switch (fmt) {
+        case QC_UNIFORM:
+            if (bits != 8 && bits != 4) return QC_ERR_UNSUPPORTED;
+            if (bad_bucket(group)) return QC_ERR_ARG;
+            if (n > 0 && !zero) return QC_ERR_ARG;
+            return QC_OK;
+        case QC_FP8_ROWWISE:
+            if (bits != 8) return QC_ERR_UNSUPPORTED;
+            if (group < 4 || group > QC_MAX_BUCKET || group % 4 != 0) return QC_ERR_UNSUPPORTED;
+            if (n % group != 0) return QC_ERR_ARG;
+            // the accumulator walks 16-element chunks inside one row
+            if (accumulate_path && bad_bucket(group)) return QC_ERR_UNSUPPORTED;
+            return QC_OK;
+        case QC_QSGD:
+            if (bits != 16) return QC_ERR_UNSUPPORTED;
+            return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
+        case QC_SIGN:
+            if (bits != 1) return QC_ERR_UNSUPPORTED;
+            return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
+        default:
+            return QC_ERR_UNSUPPORTED;
+    }
+}
+
+}  // namespace
+
+int qc_decode(int32_t fmt, const void* codes, const float* scale, const float* zero, int64_t n,
+              int32_t group, int32_t bits, float* out, qc_stream_t stream) {
+    if (n < 0) return QC_ERR_ARG;
+    const int st = check_format(fmt, n, group, bits, zero, false);
+    if (st != QC_OK) return st;
+    if (n == 0) return QC_OK;
+    if (!codes || !scale || !out) return QC_ERR_ARG;
+    if (ceil_div(n, group) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(codes) || misaligned(scale) || misaligned(zero) || misaligned(out))
+        return QC_ERR_ALIGN;
+    return launched(qc::launch_decode(fmt, codes, scale, zero, n, group, bits, out, hs(stream)));
+}
+
+int qc_dequant_accumulate(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                          int32_t m, int64_t n, int32_t group, int32_t bits, float* acc,
+                          int32_t accumulate, void* rq_codes, float* rq_scale, float* rq_zero,
+                          qc_stream_t stream) {
+    if (n < 0 || m < 1 || m > QC_MAX_WORKERS) return QC_ERR_ARG;
+    const int st = check_format(fmt, n, group, bits, zero, true);
+    if (st != QC_OK) return st;
+    const int rq_set = (rq_codes != nullptr) + (rq_scale != nullptr) + (rq_zero != nullptr);
+    if (rq_set != 0 && rq_set != 3) return QC_ERR_ARG;
+    if (rq_set == 3 && fmt != QC_UNIFORM) return QC_ERR_UNSUPPORTED;
+    if (n == 0) return QC_OK;
+    if (!codes || !scale || !acc) return QC_ERR_ARG;
+    if (ceil_div(n, group) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(codes) || misaligned(scale) || misaligned(zero) || misaligned(acc) ||
+        misaligned(rq_codes) || misaligned(rq_scale) || misaligned(rq_zero))
+        return QC_ERR_ALIGN;
+    const int64_t pbytes = qc_payload_bytes(fmt, n, group, bits);
+    return launched(qc::launch_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, pbytes,
+                                                  acc, accumulate != 0, rq_codes, rq_scale, rq_zero,
+                                                  hs(stream)));
+}
+
+int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_words,
+                     qc_stream_t stream) {
+    if (n < 0 || m < 1 || m > QC_MAX_WORKERS) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!words || !out_words) return QC_ERR_ARG;
+    if (misaligned(words) || misaligned(out_words)) return QC_ERR_ALIGN;
+    return launched(qc::launch_majority_vote(words, m, n, qc_payload_bytes(QC_SIGN, n, 64, 1),
+                                             out_words, hs(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// qc_device.hpp -- device-side building blocks shared by the libqc kernels
+// (gfx950, wave64).  Host code never includes this file.
+//
+// Numeric rule for every kernel: each fp32 operation of a codec formula
+// rounds once, to nearest even, in the order written.  Multiply-add
+// contraction is switched off twice over (the pragma below, which every
+// kernel source includes first, and -ffp-contract=off on the command line);
+// division and sqrtf keep HIP's correctly rounded defaults (the "_rn"
+// intrinsics are avoided: without extra configuration __fsqrt_rn maps to
+// the approximate native square root); fp32 denormals stay enabled.
+#pragma once
+#pragma clang fp contract(off)
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qc {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------- memory
+// Outputs are written once and not re-read by the same kernel, so they go
+// out as non-temporal stores (they should not displace inputs in L2).
+
+__device__ __forceinline__ f32x4 ld_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ u32x4 ld_u4(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st_f4(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st_u4(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_u32(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
+// ----------------------------------------------------- cross-lane reduces
+// Butterfly over aligned groups of G lanes (G a power of two <= 64).  Step
+// `off` combines lane t with lane t^off, i.e. two adjacent, equally sized,
+// contiguous blocks, so a sum built this way adds exactly the sibling
+// subtrees of a contiguous pairwise tree (fp32 addition is commutative, so
+// both partners obtain identical bits).
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v = v + __shfl_xor(v, off, WAVE);
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_min(float v) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v = fminf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, WAVE);
+    return v;
+}
+
+// Contiguous pairwise tree over N (power of two) values held in registers.
+template <int N>
+__device__ __forceinline__ float tree_sum_regs(float (&s)[N]) {
+#pragma unroll
+    for (int w = 1; w < N; w <<= 1) {
+#pragma unroll
+        for (int i = 0; i < N; i += 2 * w) s[i] = s[i] + s[i + w];
+    }
+    return s[0];
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): each round takes the
+// 32x32->64 products of counter words 0 and 2 with two fixed multipliers;
+// new words are (hi(B*c2) ^ c1 ^ k0, lo(B*c2), hi(A*c0) ^ c3 ^ k1, lo(A*c0)),
+// and the key is advanced by two Weyl increments after every round.
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+    constexpr uint32_t A = 0xD2511F53u, B = 0xCD9E8D57u;
+    constexpr uint32_t KA = 0x9E3779B9u, KB = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t pa = (uint64_t)A * c0;
+        const uint64_t pb = (uint64_t)B * c2;
+        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)pb;
+        c3 = (uint32_t)pa;
+        c0 = n0;
+        c2 = n2;
+        k0 += KA;
+        k1 += KB;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// ------------------------------------------------------------ OCP E4M3FN
+// Encode |y| <= 448 with round-to-nearest-even on the integer bit pattern.
+// Normal results (|y| >= 2^-6): add half an e4m3 ulp minus one plus the
+// kept lsb to the 20 discarded mantissa bits, shift, and rebias the
+// exponent from 127 to 7 (a carry out of the mantissa bumps the exponent,
+// which is the correct rounding).  Subnormal results: |y| * 2^9 is exact,
+// rint gives the number of 2^-9 steps (8 steps is the smallest normal,
+// whose code is also 8).  The sign bit is kept, so negative underflow
+// gives 0x80.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t normal = (rounded >> 20) - (120u << 3);
+    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sign | (a >= 0x3C800000u ? normal : sub);
+}
+
+// Exact E4M3 -> fp32: normal codes rebias the exponent by +120 and place
+// the 3 mantissa bits at the top of the fp32 mantissa; subnormal codes are
+// m * 2^-9.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t em = c & 0x7Fu;
+    const float mag = em >= 8u ? __uint_as_float((em << 20) + (120u << 23))
+                               : (float)em * 0x1p-9f;
+    return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+}
+
+// --------------------------------------------------------------- misc
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+}  // namespace qc

@@ -1,0 +1,48 @@
+// qc_launch.hpp -- internal interface between the C ABI (qc_api.cpp) and
+// the kernel sources.  Arguments arrive here already validated: pointers
+// non-NULL where required and 16-byte aligned, sizes positive, bucket a
+// power of two in [64, 65536], formats and bit widths supported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qc {
+
+// Grid-stride kernels never launch more blocks than this.
+constexpr int64_t kMaxBlocks = int64_t(1) << 20;
+
+inline int log2_exact(int64_t v) {
+    int l = 0;
+    while ((int64_t(1) << l) < v) ++l;
+    return l;
+}
+
+hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                                 void* codes, int64_t payload_bytes, float* scale, float* zero,
+                                 hipStream_t stream);
+
+hipError_t launch_encode_fp8(const float* x, int64_t rows, int32_t dim, uint8_t* codes,
+                             int64_t payload_bytes, float* scale, hipStream_t stream);
+
+hipError_t launch_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                              uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,
+                              float* norm, hipStream_t stream);
+
+hipError_t launch_encode_sign(const void* x, bool bf16, float* ef, int64_t n, int32_t bucket,
+                              uint32_t* words, int64_t payload_bytes, float* scale,
+                              hipStream_t stream);
+
+hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                         int64_t n, int32_t group, int32_t bits, float* out, hipStream_t stream);
+
+hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float* scale,
+                                     const float* zero, int32_t m, int64_t n, int32_t group,
+                                     int32_t bits, int64_t payload_bytes, float* acc,
+                                     bool accumulate, void* rq_codes, float* rq_scale,
+                                     float* rq_zero, hipStream_t stream);
+
+hipError_t launch_majority_vote(const uint32_t* words, int32_t m, int64_t n, int64_t payload_bytes,
+                                uint32_t* out_words, hipStream_t stream);
+
+}  // namespace qc

@@ -1,0 +1,235 @@
+/*
+ * qc.h -- C ABI of libqc, the quantized-communication codec for MI355X.
+ *
+ * The codec wraps a collective: the sender turns a training-precision
+ * tensor into a small wire payload before the collective and the receiver
+ * turns payloads back into fp32 and aggregates them afterwards
+ * ("Quantized Communication for Distributed Training", section "Where
+ * Quantization Sits"; "Gradient quantization for communication", section
+ * "How Gradient Quantization Works").  This library is the per-GPU part:
+ * it never communicates.
+ *
+ * Common rules for every entry point
+ * ----------------------------------
+ *  - Array arguments are DEVICE pointers on the current HIP device,
+ *    allocated and owned by the caller, 16-byte aligned, and must not
+ *    overlap each other (the error-feedback buffer is the one array that is
+ *    both read and written).
+ *  - Every call validates its arguments on the host first; on any error it
+ *    returns the status code with nothing enqueued and nothing written.
+ *    Otherwise it only enqueues kernels on `stream` (NULL = the default
+ *    stream) and returns QC_OK; results are ready once the stream is
+ *    synchronized.  The library allocates no memory and keeps no state
+ *    between calls, so calls on different streams are independent.
+ *  - n == 0 (or rows == 0) is a valid empty call: QC_OK, nothing enqueued.
+ *  - Buckets: `bucket` consecutive elements share one set of statistics.
+ *    It must be a power of two in [64, 65536].  The last bucket may be
+ *    short; it gets its own statistics.  nb = ceil(n / bucket).
+ *  - Payloads: a payload of n codes occupies qc_payload_bytes() bytes
+ *    (code bytes rounded up to 16).  Encoders write every byte of it;
+ *    bytes after the last code are zero.  4-bit codes are packed eight to a
+ *    little-endian 32-bit word, element i in bits 4*(i%8)..4*(i%8)+3 of word
+ *    i/8; 1-bit codes thirty-two to a word, element i in bit i%32 of word
+ *    i/32.  M payloads of one kind are stored back to back, payload w at
+ *    byte offset w * qc_payload_bytes(), its per-bucket fp32 statistics at
+ *    element offset w * nb of the scale/zero arrays.
+ *  - Arithmetic is IEEE fp32 with round-to-nearest-even, no fused
+ *    multiply-add in the codec formulas, correctly rounded division and
+ *    square root, and denormals preserved, so results are bit-for-bit
+ *    reproducible.  Inputs must be finite.
+ */
+#ifndef QC_H
+#define QC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same underlying type as hipStream_t, so a hipStream_t passes unchanged. */
+typedef struct ihipStream_t* qc_stream_t;
+
+enum qc_status {
+    QC_OK = 0,
+    QC_ERR_ARG = 1,          /* NULL pointer, negative size, bad bucket/m/offset */
+    QC_ERR_ALIGN = 2,        /* a device pointer is not 16-byte aligned */
+    QC_ERR_UNSUPPORTED = 3,  /* bits/levels/format/dim this entry point lacks */
+    QC_ERR_LAUNCH = 4        /* the HIP runtime refused the kernel launch */
+};
+
+enum qc_format { QC_UNIFORM = 0, QC_FP8_ROWWISE = 1, QC_QSGD = 2, QC_SIGN = 3 };
+enum qc_dtype { QC_F32 = 0, QC_BF16 = 1 };
+
+#define QC_MIN_BUCKET 64
+#define QC_MAX_BUCKET 65536
+#define QC_MAX_WORKERS 65535
+
+/*
+ * Uniform (affine) quantization with optional error feedback.
+ * ("Quantization for Communication", section "Quantization Schemes",
+ * uniform quantization; section "Error Feedback for Quantization", the
+ * implementation steps.)
+ *
+ * Per bucket, v = ef + x (or v = x when ef is NULL); mn/mx are the bucket's
+ * min/max of v (a -0 extreme becomes +0); scale = (mx - mn) / (2^bits - 1);
+ * zero = mn; code = rint((v - mn) / scale) clamped to [0, 2^bits - 1]
+ * (all codes 0 when scale == 0); DQ = code*scale + zero; and, with ef,
+ * ef = v - DQ afterwards.
+ *
+ *   x      fp32[n], read.
+ *   ef     fp32[n], read and written in place, or NULL (no feedback).
+ *   bits   8 (one byte per code) or 4 (eight codes per word).
+ *   codes  qc_payload_bytes(QC_UNIFORM, n, bucket, bits) bytes, written.
+ *   scale  fp32[nb] written; zero fp32[nb] written.
+ * Errors: ARG (NULL x/codes/scale/zero, n < 0, bad bucket), ALIGN,
+ *         UNSUPPORTED (bits not 4 or 8).
+ */
+int qc_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                      void* codes, float* scale, float* zero, qc_stream_t stream);
+
+/*
+ * Rowwise FP8 (OCP E4M3FN) for embedding-lookup payloads: one byte per
+ * value plus one fp32 scale per row ("Quantized Communication for
+ * Distributed Training", sections "Numeric Example" and "Pinterest QComms
+ * Example").
+ *
+ * Per row: scale = max|x| / 448; code = E4M3(clamp(x / scale, -448, 448)),
+ * rounded to nearest even, sign kept on underflow, never NaN; all codes 0
+ * when scale == 0.  DQ = E4M3value(code) * scale.
+ *
+ *   x      fp32[rows * dim] row-major, read.
+ *   dim    elements per row, a multiple of 4 in [4, 65536].
+ *   codes  qc_payload_bytes(QC_FP8_ROWWISE, rows*dim, dim, 8) bytes, written.
+ *   scale  fp32[rows], written.
+ * Errors: ARG (NULL pointer, rows < 0), ALIGN, UNSUPPORTED (dim).
+ */
+int qc_encode_fp8_rowwise(const float* x, int64_t rows, int32_t dim, uint8_t* codes,
+                          float* scale, qc_stream_t stream);
+
+/*
+ * QSGD: stochastic quantization to s = 16 codes (4 bits: 32/log2(16) = 8x)
+ * with optional error feedback ("Quantization for Communication", sections
+ * "Quantized SGD Algorithms" and "Quantization Schemes", stochastic
+ * quantization; "Gradient Compression and Quantised Collectives", section
+ * "Why sparsification fights the all-reduce", unbiased quantisation).
+ *
+ * Per bucket, v as above; norm = sqrt(sum of v^2), the sum taken as a
+ * contiguous pairwise tree over the bucket (padded with +0); d = norm / 7.
+ * A code is a sign bit (bit 3) and a level l in 0..7 (bits 0-2) standing
+ * for l*d.  With t = |v| / d, l = floor(t) + (u < t - floor(t)), capped at
+ * 7, where u = (r >> 8) * 2^-24 and r is word g%4 of Philox4x32-10 with
+ * key (seed low 32 bits, seed high 32 bits) and counter (g/4 low, g/4
+ * high, 0, 0), g = elem_offset + element index.  Level 0 gives code 0 and
+ * DQ +0; all codes are 0 when d == 0.  With ef: ef = v - DQ.
+ *
+ *   x, ef       as for qc_encode_uniform.
+ *   levels      must be 16.
+ *   seed        64-bit generator key; vary it per step.
+ *   elem_offset global index of x[0] (for a shard of a larger tensor);
+ *               a multiple of 4.
+ *   words       qc_payload_bytes(QC_QSGD, n, bucket, 16) bytes, written.
+ *   norm        fp32[nb], written (the decoder recomputes d = norm / 7).
+ * Errors: ARG (NULL pointer, n < 0, bad bucket, elem_offset % 4 != 0),
+ *         ALIGN, UNSUPPORTED (levels != 16).
+ */
+int qc_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, int32_t levels,
+                   uint64_t seed, uint64_t elem_offset, uint32_t* words, float* norm,
+                   qc_stream_t stream);
+
+/*
+ * 1-bit sign quantization with a per-bucket scale and optional error
+ * feedback ("Quantization for Communication", sections "Bit-Width
+ * Selection" and "Quantized SGD Algorithms", SignSGD; "Gradient
+ * Compression and Quantised Collectives", section "Error feedback is the
+ * component that makes it work").
+ *
+ * Per bucket, v = ef + x (bf16 x widened exactly to fp32); scale = (sum of
+ * |v|, contiguous pairwise tree) / (valid elements in the bucket);
+ * bit = (v < 0); DQ = bit ? -scale : +scale; with ef: ef = v - DQ.
+ *
+ *   x      QC_F32: fp32[n]; QC_BF16: bf16[n] (uint16 bit patterns), read.
+ *   xtype  QC_F32 or QC_BF16.
+ *   ef     fp32[n] or NULL.
+ *   words  qc_payload_bytes(QC_SIGN, n, bucket, 1) bytes, written.
+ *   scale  fp32[nb], written.
+ * Errors: ARG (NULL pointer, n < 0, bad bucket, bad xtype), ALIGN.
+ */
+int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t bucket,
+                   uint32_t* words, float* scale, qc_stream_t stream);
+
+/*
+ * Decode one payload to fp32 (receive side: "Quantized Communication for
+ * Distributed Training", section "Where Quantization Sits").
+ *
+ *   fmt    QC_UNIFORM: bits 8 or 4, scale and zero per bucket of `group`;
+ *          QC_FP8_ROWWISE: group = dim, scale per row, zero unused;
+ *          QC_QSGD: bits = 16 (levels), scale = the norm array, zero unused;
+ *          QC_SIGN: bits = 1, scale per bucket, zero unused.
+ *   codes  the payload, read.   out  fp32[n], written.
+ * DQ is the formula stated for the matching encoder.
+ * Errors: ARG (NULL pointer, n < 0, bad group, n % dim != 0 for FP8),
+ *         ALIGN, UNSUPPORTED (fmt/bits).
+ */
+int qc_decode(int32_t fmt, const void* codes, const float* scale, const float* zero, int64_t n,
+              int32_t group, int32_t bits, float* out, qc_stream_t stream);
+
+/*
+ * Receive-side quantized accumulation in fp32 ("Quantization for
+ * Communication", section "Quantization-Aware All-Reduce", quantized
+ * accumulation; "Gradient quantization for communication", section "How
+ * Gradient Quantization Works": dequantize, then aggregate).
+ *
+ * acc[i] = (accumulate ? acc[i] : +0) + DQ_0[i] + DQ_1[i] + ... + DQ_{m-1}[i],
+ * added in worker order, for m payloads stored back to back (see the
+ * common rules).  If rq_codes is non-NULL the summed vector is then
+ * requantized with qc_encode_uniform's rule (no error feedback, same
+ * bits and bucket = group) into rq_codes/rq_scale/rq_zero, in the same
+ * pass.
+ *
+ *   fmt/group/bits as for qc_decode.  m in [1, QC_MAX_WORKERS].
+ *   codes   m payloads, read.  scale/zero fp32[m * nb], read.
+ *   acc     fp32[n], read if accumulate != 0, written.
+ *   rq_*    NULL, or (fmt == QC_UNIFORM only) a payload of
+ *           qc_payload_bytes(QC_UNIFORM, n, group, bits) bytes and fp32[nb]
+ *           scale and zero arrays, written.
+ * Errors: ARG (NULL pointer, bad m/n/group, rq_* partly NULL), ALIGN,
+ *         UNSUPPORTED (fmt/bits, requantization of a non-uniform format).
+ */
+int qc_dequant_accumulate(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                          int32_t m, int64_t n, int32_t group, int32_t bits, float* acc,
+                          int32_t accumulate, void* rq_codes, float* rq_scale, float* rq_zero,
+                          qc_stream_t stream);
+
+/*
+ * signSGD aggregation by majority vote ("Quantization for Communication",
+ * section "Quantized SGD Algorithms", SignSGD; "Gradient Compression and
+ * Quantised Collectives", section "Why sparsification fights the
+ * all-reduce", one-bit methods).
+ *
+ * Output bit p is 1 iff more than m/2 of the m sign payloads have bit p
+ * set (a tie at even m gives 0, the "+" of sign(0)).
+ *
+ *   words      m sign payloads of n bits, back to back, read.
+ *   out_words  one sign payload, qc_payload_bytes(QC_SIGN, n, 64, 1) bytes,
+ *              written (padding zero).
+ * Errors: ARG (NULL pointer, n < 0, m outside [1, QC_MAX_WORKERS]), ALIGN.
+ */
+int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_words,
+                     qc_stream_t stream);
+
+/*
+ * Bytes of one payload of n elements: the code bytes (n for INT8/FP8,
+ * 4*ceil(n/8) for 4-bit formats, 4*ceil(n/32) for sign) rounded up to 16.
+ * `group` is accepted for symmetry and does not change the size.  Returns
+ * -1 for an unknown format/bits or n < 0.
+ */
+int64_t qc_payload_bytes(int32_t fmt, int64_t n, int32_t group, int32_t bits);
+
+/* Static string naming a status code. */
+const char* qc_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QC_H */

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point include/qc.h declares, sizes payloads as documented, and rejects bad
+arguments with the documented status before touching the HIP runtime (so
+these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qc.h")
+
+
+@pytest.fixture(scope="module")
+def qc():
+    import embedding_communication_codecs_amd as q
+
+    if not os.path.exists(q.binding.LIB_PATH):
+        pytest.skip("libqc.so not built (python -m embedding_communication_codecs_amd.build)")
+    q.lib()
+    return q
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points(qc):
+    names = declared_functions()
+    assert set(names) == set(qc.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(qc):
+    out = subprocess.run(["nm", "-D", "--defined-only", qc.binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(qc.lib(), name) is not None
+
+
+def test_payload_bytes_matches_oracle(qc, ora):
+    for n in (0, 1, 3, 4, 15, 16, 17, 31, 32, 33, 127, 128, 129, 1000, 65536, 10**9):
+        assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 8) == ora.payload_bytes(ora.UNIFORM, n, 8)
+        assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 4) == ora.payload_bytes(ora.UNIFORM, n, 4)
+        assert qc.qc_payload_bytes(qc.QC_FP8_ROWWISE, n, 4, 8) == ora.payload_bytes(ora.FP8_ROWWISE, n)
+        assert qc.qc_payload_bytes(qc.QC_QSGD, n, 512, 16) == ora.payload_bytes(ora.QSGD, n, 4)
+        assert qc.qc_payload_bytes(qc.QC_SIGN, n, 4096, 1) == ora.payload_bytes(ora.SIGN, n, 1)
+    assert qc.qc_payload_bytes(qc.QC_UNIFORM, 10, 64, 3) == -1
+    assert qc.qc_payload_bytes(9, 10, 64, 8) == -1
+    assert qc.qc_payload_bytes(qc.QC_UNIFORM, -1, 64, 8) == -1
+
+
+def test_status_strings(qc):
+    for s in range(5):
+        assert qc.qc_status_str(s).startswith("QC_")
+    assert "unknown" in qc.qc_status_str(99)
+
+
+# Fake device addresses: validation rejects the call before any use.
+A = 1 << 20           # 16-byte aligned
+MIS = (1 << 20) + 4   # misaligned
+NULL = None
+
+
+def call(qc, name, *args):
+    return getattr(qc.lib(), name)(*args)
+
+
+def test_encode_uniform_errors(qc):
+    f = "qc_encode_uniform"
+    ok = (A, A, 1000, 256, 8, A, A, A, None)
+    assert call(qc, f, NULL, *ok[1:]) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, -1, 256, 8, A, A, A, None) == qc.QC_ERR_ARG
+    for bad in (0, 32, 100, 96, 131072, -64):
+        assert call(qc, f, A, A, 1000, bad, 8, A, A, A, None) == qc.QC_ERR_ARG, bad
+    for bits in (0, 1, 2, 3, 5, 16):
+        assert call(qc, f, A, A, 1000, 256, bits, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, A, A, 1000, 256, 8, NULL, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 256, 8, A, NULL, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 256, 8, A, A, NULL, None) == qc.QC_ERR_ARG
+    for pos in (0, 1, 5, 6, 7):
+        args = list(ok)
+        args[pos] = MIS
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    # empty input is a valid no-op, even with NULL buffers
+    assert call(qc, f, NULL, NULL, 0, 256, 8, NULL, NULL, NULL, None) == qc.QC_OK
+
+
+def test_encode_fp8_errors(qc):
+    f = "qc_encode_fp8_rowwise"
+    assert call(qc, f, A, -1, 128, A, A, None) == qc.QC_ERR_ARG
+    for dim in (0, 2, 6, 130, 65540):
+        assert call(qc, f, A, 10, dim, A, A, None) == qc.QC_ERR_UNSUPPORTED, dim
+    assert call(qc, f, NULL, 10, 128, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 10, 128, NULL, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 10, 128, A, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, MIS, 10, 128, A, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, A, 10, 128, MIS, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, 0, 128, NULL, NULL, None) == qc.QC_OK
+
+
+def test_encode_qsgd_errors(qc):
+    f = "qc_encode_qsgd"
+    assert call(qc, f, A, A, 1000, 512, 16, 1, 2, A, A, None) == qc.QC_ERR_ARG  # offset % 4
+    assert call(qc, f, A, A, 1000, 500, 16, 1, 0, A, A, None) == qc.QC_ERR_ARG
+    for lv in (2, 4, 8, 15, 32):
+        assert call(qc, f, A, A, 1000, 512, lv, 1, 0, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, A, A, 1000, 512, 16, 1, 0, NULL, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, MIS, 1000, 512, 16, 1, 0, A, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, NULL, 0, 512, 16, 1, 0, NULL, NULL, None) == qc.QC_OK
+
+
+def test_encode_sign_errors(qc):
+    f = "qc_encode_sign"
+    assert call(qc, f, A, 2, A, 1000, 4096, A, A, None) == qc.QC_ERR_ARG  # xtype
+    assert call(qc, f, A, 1, A, 1000, 4095, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 1, A, 1000, 4096, A, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 1, A, 1000, 4096, MIS, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, 1, NULL, 0, 4096, NULL, NULL, None) == qc.QC_OK
+
+
+def test_decode_errors(qc):
+    f = "qc_decode"
+    assert call(qc, f, 7, A, A, A, 100, 64, 8, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_UNIFORM, A, A, A, 100, 64, 2, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_UNIFORM, A, A, NULL, 100, 64, 8, A, None) == qc.QC_ERR_ARG  # zero needed
+    assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 100, 128, 8, A, None) == qc.QC_ERR_ARG  # n % dim
+    assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 128, 6, 8, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_QSGD, A, A, NULL, 100, 512, 4, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_SIGN, A, A, NULL, 100, 512, 8, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_SIGN, A, A, NULL, 100, 300, 1, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, qc.QC_SIGN, A, A, NULL, 100, 512, 1, MIS, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, qc.QC_SIGN, NULL, NULL, NULL, 0, 512, 1, NULL, None) == qc.QC_OK
+
+
+def test_dequant_accumulate_errors(qc):
+    f = "qc_dequant_accumulate"
+    U = qc.QC_UNIFORM
+    assert call(qc, f, U, A, A, A, 0, 100, 64, 8, A, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, U, A, A, A, 65536, 100, 64, 8, A, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, U, A, A, A, 4, 100, 64, 8, A, 0, A, NULL, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, qc.QC_SIGN, A, A, NULL, 4, 100, 64, 1, A, 0, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 4, 96 * 3, 96, 8, A, 0, NULL, NULL, NULL,
+                None) == qc.QC_ERR_UNSUPPORTED  # rows for accumulation: power-of-two dims
+    assert call(qc, f, U, A, A, A, 4, 100, 64, 8, MIS, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, U, A, A, A, 4, 100, 64, 8, A, 0, A, A, MIS, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, U, NULL, NULL, NULL, 4, 0, 64, 8, NULL, 0, NULL, NULL, NULL, None) == qc.QC_OK
+
+
+def test_majority_vote_errors(qc):
+    f = "qc_majority_vote"
+    assert call(qc, f, A, 0, 100, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 70000, 100, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, NULL, 3, 100, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 3, 100, MIS, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, 3, 0, NULL, None) == qc.QC_OK
+
+
+def test_binding_rejects_undersized_buffers_before_the_library(qc):
+    """The Python binding checks tensor capacities; CPU tensors are refused
+    outright (these raise before any library call)."""
+    import torch
+
+    x = torch.zeros(10)
+    with pytest.raises(ValueError):
+        qc.qc_encode_uniform(x, None, 10, 64, 8, x, x, x, stream=0)

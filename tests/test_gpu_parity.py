@@ -1,0 +1,443 @@
+"""GPU parity: every entry point, called through the C ABI, against the CPU
+oracle on the same seeded inputs, at sizes that span several tiles and a
+ragged tail, plus the degenerate cases.  Codes, scales, packed words,
+decoded values and residuals must be bit-identical; sums over workers must
+be within 1e-5 of the sum of |terms| (and are checked bit-exact too, since
+the kernel adds in the oracle's order)."""
+import math
+
+import numpy as np
+import pytest
+
+from embedding_communication_codecs_amd import synth
+from gpu_util import Out, bits_equal, dev, dev_ef, first_diff, need_gpu, out_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qc():
+    return need_gpu()
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+# ================================================================ uniform
+
+
+def run_uniform(qc, x, ef, bucket, bits):
+    n = x.size
+    nb = qc.nbuckets(n, bucket)
+    codes = Out(qc.payload_bytes(qc.QC_UNIFORM, n, bucket, bits))
+    scale, zero = out_f32(nb), out_f32(nb)
+    qc.qc_encode_uniform(dev(x), None if ef is None else ef.t, n, bucket, bits, codes.t, scale.t, zero.t)
+    sync()
+    return codes, scale, zero
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536])
+def test_uniform_parity_ef_steps(qc, ora, bucket, bits):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(3):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=1000 * bucket + step)
+        codes, scale, zero = run_uniform(qc, g, ef_d, bucket, bits)
+        p, s, z = ora.encode_uniform(g, ef_h, bucket, bits)
+        assert bits_equal(codes.host(), p), (step, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(zero.f32(), z), first_diff(zero.f32(), z)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    out = out_f32(n)
+    qc.qc_decode(qc.QC_UNIFORM, codes.t, scale.t, zero.t, n, bucket, bits, out.t)
+    sync()
+    want = ora.decode_uniform(p, s, z, n, bucket, bits)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 63, 64, 65, 1000, 4096 * 5 + 3])
+def test_uniform_parity_ragged_no_ef(qc, ora, n, bits):
+    x = synth.host_normal(n, 1.0, seed=n)
+    codes, scale, zero = run_uniform(qc, x, None, 256, bits)
+    p, s, z = ora.encode_uniform(x, None, 256, bits)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+
+
+def test_uniform_special_values(qc, ora):
+    B = 64
+    rows = [
+        np.full(B, 0.5, np.float32),                                  # constant bucket
+        np.array([-0.0] * 32 + [0.0] * 32, np.float32),               # signed zeros
+        np.array([1e-45, -1e-45, 3e-39, -2e-39] * 16, np.float32),    # subnormals
+        np.linspace(-1, 1, B).astype(np.float32),
+        (np.arange(B, dtype=np.float32) - 7) * np.float32(1.0 / 255),  # codes near ties
+        np.array([1e30, -1e30] + [0.0] * 62, np.float32),             # huge range
+    ]
+    x = np.concatenate(rows)
+    for bits in (8, 4):
+        ef_h = synth.host_normal(x.size, 1e-7, seed=4).astype(np.float32)
+        ef_d = dev_ef(ef_h)
+        codes, scale, zero = run_uniform(qc, x, ef_d, B, bits)
+        p, s, z = ora.encode_uniform(x, ef_h, B, bits)
+        assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+        assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+
+
+# ==================================================================== fp8
+
+
+def run_fp8(qc, x, rows, dim):
+    codes = Out(qc.payload_bytes(qc.QC_FP8_ROWWISE, rows * dim, dim, 8))
+    scale = out_f32(rows)
+    qc.qc_encode_fp8_rowwise(dev(x), rows, dim, codes.t, scale.t)
+    sync()
+    return codes, scale
+
+
+@pytest.mark.parametrize("dim", [4, 8, 16, 32, 64, 128, 256, 12, 96, 1000, 4096])
+@pytest.mark.parametrize("rows", [1, 7, 1003])
+def test_fp8_parity(qc, ora, rows, dim):
+    x = synth.host_embedding_rows(rows, dim, 0.05, 0.01, 50.0, seed=rows * 7919 + dim)
+    if rows > 3:
+        x[dim: 2 * dim] = 0.0  # an all-zero row
+    codes, scale = run_fp8(qc, x, rows, dim)
+    p, s = ora.encode_fp8_rowwise(x, rows, dim)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+    out = out_f32(rows * dim)
+    qc.qc_decode(qc.QC_FP8_ROWWISE, codes.t, scale.t, None, rows * dim, dim, 8, out.t)
+    sync()
+    want = ora.decode_fp8_rowwise(p, s, rows, dim)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
+def test_fp8_rounding_edges(qc, ora):
+    """Rows whose amax is 448 have scale exactly 1, so each code is the
+    E4M3 conversion of the value itself: ties, binade edges, subnormals,
+    signed zeros and tiny negatives."""
+    dim = 128
+    vals = [448.0, -448.0, 232.0, 248.0, 1.0625, 1.1875, 2.0 ** -6, 2.0 ** -7, 2.0 ** -10,
+            3 * 2.0 ** -10, 15 * 2.0 ** -10, 2.0 ** -10 * 1.0000001, -1e-30, -0.0, 0.0, 447.99,
+            416.0, 432.0, 240.0, 0.0009765625, 1e-45, -1e-45]
+    rng = np.random.default_rng(1)
+    rows = []
+    for r in range(64):
+        row = rng.uniform(-448, 448, dim).astype(np.float32)
+        row[: len(vals)] = vals
+        row[0] = 448.0
+        # mantissa-boundary values in many binades
+        e = rng.integers(-10, 8, dim - len(vals))
+        m = rng.integers(0, 16, dim - len(vals))
+        row[len(vals):] = np.ldexp(1 + m / 16.0, e).astype(np.float32) * np.where(r % 2, -1, 1)
+        row[1] = 448.0
+        rows.append(row)
+    x = np.concatenate(rows).astype(np.float32)
+    codes, scale = run_fp8(qc, x, 64, dim)
+    p, s = ora.encode_fp8_rowwise(x, 64, dim)
+    assert np.all(s == 1.0)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_fp8_conversion_sweep(qc, ora, seed):
+    """4M random fp32 bit patterns in [-448, 448] through rows with scale 1."""
+    dim, rows = 256, 16384
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 0x43E00001, rows * dim, dtype=np.uint32)
+    bits |= (rng.integers(0, 2, rows * dim, dtype=np.uint32) << 31)
+    x = bits.view(np.float32).copy()
+    x.reshape(rows, dim)[:, 0] = 448.0
+    codes, scale = run_fp8(qc, x, rows, dim)
+    p, s = ora.encode_fp8_rowwise(x, rows, dim)
+    assert np.all(s == 1.0)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+
+
+# =================================================================== qsgd
+
+
+def run_qsgd(qc, x, ef, bucket, seed, offset):
+    n = x.size
+    words = Out(qc.payload_bytes(qc.QC_QSGD, n, bucket, 16))
+    norm = out_f32(qc.nbuckets(n, bucket))
+    qc.qc_encode_qsgd(dev(x), None if ef is None else ef.t, n, bucket, 16, seed, offset, words.t, norm.t)
+    sync()
+    return words, norm
+
+
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 65536])
+def test_qsgd_parity_ef_steps(qc, ora, bucket):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(2):
+        g = synth.host_laplace(n, 1e-4, seed=3001 + step + bucket)
+        seed = 0x5153474400000001 + step
+        words, norm = run_qsgd(qc, g, ef_d, bucket, seed, 0)
+        p, nr = ora.encode_qsgd(g, ef_h, bucket, seed, 0)
+        assert bits_equal(words.host(), p), (step, first_diff(words.host(), p))
+        assert bits_equal(norm.f32(), nr), first_diff(norm.f32(), nr)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    out = out_f32(n)
+    qc.qc_decode(qc.QC_QSGD, words.t, norm.t, None, n, bucket, 16, out.t)
+    sync()
+    want = ora.decode_qsgd(p, nr, n, bucket)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
+@pytest.mark.parametrize("offset", [0, 4, 4 * 123456789, 2**40])
+@pytest.mark.parametrize("n", [1, 5, 511, 513, 2000])
+def test_qsgd_offsets_and_tails(qc, ora, n, offset):
+    x = synth.host_laplace(n, 1e-4, seed=n + 11)
+    words, norm = run_qsgd(qc, x, None, 512, 0xFEEDFACECAFEBEEF, offset)
+    p, nr = ora.encode_qsgd(x, None, 512, 0xFEEDFACECAFEBEEF, offset)
+    assert bits_equal(words.host(), p), first_diff(words.host(), p)
+    assert bits_equal(norm.f32(), nr)
+
+
+def test_qsgd_special_values(qc, ora):
+    B = 64
+    x = np.concatenate([
+        np.zeros(B, np.float32),                                           # d == 0
+        np.array([-7.0] + [0.0] * 63, np.float32),                         # on grid
+        np.array([2.0, -3.0, 6.0] + [0.0] * 61, np.float32),               # on grid, norm 7
+        np.array([1e-45] * 64, np.float32),                                # subnormal norm
+        np.array([-0.0] * 32 + [1e-3] * 32, np.float32),
+    ])
+    ef_h = np.zeros(x.size, np.float32)
+    ef_d = dev_ef(ef_h)
+    words, norm = run_qsgd(qc, x, ef_d, B, 99, 0)
+    p, nr = ora.encode_qsgd(x, ef_h, B, 99, 0)
+    assert bits_equal(words.host(), p) and bits_equal(norm.f32(), nr)
+    assert bits_equal(ef_d.f32(), ef_h)
+
+
+# =================================================================== sign
+
+
+def run_sign(qc, x, ef, bucket):
+    n = x.size
+    words = Out(qc.payload_bytes(qc.QC_SIGN, n, bucket, 1))
+    scale = out_f32(qc.nbuckets(n, bucket))
+    xt = qc.QC_BF16 if x.dtype == np.uint16 else qc.QC_F32
+    qc.qc_encode_sign(dev(x), xt, ef.t if ef is not None else None, n, bucket, words.t, scale.t)
+    sync()
+    return words, scale
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 65536])
+def test_sign_parity_ef_steps(qc, ora, bucket, dtype):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(2):
+        g = synth.host_normal(n, 1e-3, seed=4001 + step + bucket)
+        if dtype == "bf16":
+            g = synth.host_bf16_bits(g)
+        words, scale = run_sign(qc, g, ef_d, bucket)
+        p, s = ora.encode_sign(g, ef_h, bucket)
+        assert bits_equal(words.host(), p), (step, first_diff(words.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    out = out_f32(n)
+    qc.qc_decode(qc.QC_SIGN, words.t, scale.t, None, n, bucket, 1, out.t)
+    sync()
+    want = ora.decode_sign(p, s, n, bucket)
+    assert bits_equal(out.f32(), want)
+
+
+@pytest.mark.parametrize("n", [1, 7, 31, 32, 33, 64, 65, 100, 129])
+def test_sign_small_bucket_tails(qc, ora, n):
+    """64-element buckets: the padded payload extends past the last bucket."""
+    x = synth.host_normal(n, 1.0, seed=n)
+    x[::3] = -0.0
+    words, scale = run_sign(qc, x, None, 64)
+    p, s = ora.encode_sign(x, None, 64)
+    assert bits_equal(words.host(), p), first_diff(words.host(), p)
+    assert bits_equal(scale.f32(), s)
+
+
+# ============================================================= accumulate
+
+
+def make_payloads(ora, fmt, m, n, group, seed):
+    parts, sc, ze = [], [], []
+    for w in range(m):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=seed + w)
+        if fmt == "u8" or fmt == "u4":
+            p, s, z = ora.encode_uniform(g, None, group, 8 if fmt == "u8" else 4)
+            ze.append(z)
+        elif fmt == "fp8":
+            p, s = ora.encode_fp8_rowwise(g, n // group, group)
+        elif fmt == "qsgd":
+            p, s = ora.encode_qsgd(g, None, group, seed + w)
+        else:
+            p, s = ora.encode_sign(g, None, group)
+        parts.append(p)
+        sc.append(s)
+    zero = np.concatenate(ze) if ze else None
+    return np.concatenate(parts), np.concatenate(sc), zero
+
+
+FMT = {"u8": (0, 8), "u4": (0, 4), "fp8": (1, 8), "qsgd": (2, 16), "sign": (3, 1)}
+ORA_FMT = {"u8": 0, "u4": 0, "fp8": 1, "qsgd": 2, "sign": 3}
+
+
+@pytest.mark.parametrize("fmt,group", [("u8", 64), ("u8", 2048), ("u8", 4096), ("u8", 8192),
+                                       ("u4", 256), ("u4", 2048), ("fp8", 128), ("fp8", 64),
+                                       ("qsgd", 512), ("sign", 4096), ("sign", 64)])
+@pytest.mark.parametrize("m", [1, 3, 5, 16])
+def test_dequant_accumulate_parity(qc, ora, fmt, group, m):
+    n = 3 * group + (0 if fmt == "fp8" else 37)
+    code, bits = FMT[fmt]
+    payloads, scale, zero = make_payloads(ora, fmt, m, n, group, seed=5000 + m)
+    obits = 8 if fmt == "fp8" else (4 if fmt in ("u4", "qsgd") else (1 if fmt == "sign" else 8))
+    want = ora.dequant_accumulate(ORA_FMT[fmt], payloads, scale, zero, m, n, group, obits)
+    acc = out_f32(n)
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), None if zero is None else dev(zero), m, n,
+                             group, bits, acc.t, False)
+    sync()
+    got = acc.f32()
+    assert bits_equal(got, want), first_diff(got, want)
+    # and accumulate=1 continues from the current contents
+    start = synth.host_normal(n, 1e-3, seed=77)
+    acc.t.copy_(dev(start))
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), None if zero is None else dev(zero), m, n,
+                             group, bits, acc.t, True)
+    sync()
+    want2 = ora.dequant_accumulate(ORA_FMT[fmt], payloads, scale, zero, m, n, group, obits, acc=start)
+    assert bits_equal(acc.f32(), want2), first_diff(acc.f32(), want2)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("group", [64, 512, 2048, 8192])
+def test_dequant_accumulate_requant(qc, ora, group, bits):
+    m, n = 6, 3 * group + 21
+    fmt = "u8" if bits == 8 else "u4"
+    payloads, scale, zero = make_payloads(ora, fmt, m, n, group, seed=9000)
+    acc = out_f32(n)
+    nb = qc.nbuckets(n, group)
+    rq = Out(qc.payload_bytes(qc.QC_UNIFORM, n, group, bits))
+    rqs, rqz = out_f32(nb), out_f32(nb)
+    qc.qc_dequant_accumulate(0, dev(payloads), dev(scale), dev(zero), m, n, group, bits, acc.t, False,
+                             rq.t, rqs.t, rqz.t)
+    sync()
+    want = ora.dequant_accumulate(0, payloads, scale, zero, m, n, group, bits)
+    assert bits_equal(acc.f32(), want)
+    p, s, z = ora.encode_uniform(want, None, group, bits)
+    assert bits_equal(rq.host(), p), first_diff(rq.host(), p)
+    assert bits_equal(rqs.f32(), s) and bits_equal(rqz.f32(), z)
+
+
+def test_accumulate_tolerance_contract(qc, ora):
+    """The stated contract: |acc - exact| <= 1e-5 * sum |terms|."""
+    m, n, group = 16, 4096 + 5, 2048
+    payloads, scale, zero = make_payloads(ora, "u8", m, n, group, seed=31)
+    acc = out_f32(n)
+    qc.qc_dequant_accumulate(0, dev(payloads), dev(scale), dev(zero), m, n, group, 8, acc.t, False)
+    sync()
+    pb = ora.payload_bytes(0, n, 8)
+    nb = ora.nbuckets(n, group)
+    terms = np.stack([ora.decode_uniform(payloads[w * pb:(w + 1) * pb], scale[w * nb:(w + 1) * nb],
+                                         zero[w * nb:(w + 1) * nb], n, group, 8) for w in range(m)])
+    T = terms.astype(np.float64)
+    exact = np.array([math.fsum(T[:, i]) for i in range(n)])
+    assert np.all(np.abs(acc.f32() - exact) <= 1e-5 * np.abs(T).sum(axis=0))
+
+
+# ================================================================= vote
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 15, 16, 17, 64, 255, 256, 1000])
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 4096 * 3 + 7])
+def test_majority_vote_parity(qc, ora, m, n):
+    pb = qc.payload_bytes(qc.QC_SIGN, n, 64, 1)
+    arena = np.concatenate([synth.host_words(pb // 4, 4100 + w).view(np.uint8) for w in range(m)])
+    out = Out(pb)
+    qc.qc_majority_vote(dev(arena).view(__import__("torch").int32), m, n, out.t.view(__import__("torch").int32))
+    sync()
+    want = ora.majority_vote(arena, m, n)
+    assert bits_equal(out.host(), want), first_diff(out.host(), want)
+
+
+def test_vote_of_encoded_signs(qc, ora):
+    """Sign payloads produced by the encoder, then voted and decoded."""
+    import torch
+
+    m, n, B = 7, 10000, 4096
+    pb = qc.payload_bytes(qc.QC_SIGN, n, B, 1)
+    arena = Out(m * pb)
+    parts = []
+    base = synth.host_normal(n, 1e-3, seed=1)
+    for w in range(m):
+        g = (base + synth.host_normal(n, 1e-3, seed=100 + w)).astype(np.float32)
+        p, _ = ora.encode_sign(g, None, B)
+        parts.append(p)
+        words = arena.t[w * pb:(w + 1) * pb].view(torch.int32)
+        scale = out_f32(qc.nbuckets(n, B))
+        qc.qc_encode_sign(dev(g), qc.QC_F32, None, n, B, words, scale.t)
+    out = Out(pb)
+    qc.qc_majority_vote(arena.t.view(torch.int32), m, n, out.t.view(torch.int32))
+    sync()
+    assert bits_equal(arena.host(), np.concatenate(parts))
+    assert bits_equal(out.host(), ora.majority_vote(np.concatenate(parts), m, n))
+
+
+# ============================================================ degenerate
+
+
+def test_empty_inputs_write_nothing(qc):
+    o = Out(64)
+    f = out_f32(16)
+    qc.qc_encode_uniform(f.t, None, 0, 64, 8, o.t, f.t, f.t)
+    qc.qc_encode_fp8_rowwise(f.t, 0, 128, o.t, f.t)
+    qc.qc_encode_qsgd(f.t, None, 0, 512, 16, 1, 0, o.t, f.t)
+    qc.qc_encode_sign(f.t, qc.QC_F32, None, 0, 64, o.t, f.t)
+    qc.qc_decode(qc.QC_SIGN, o.t, f.t, None, 0, 64, 1, f.t)
+    qc.qc_dequant_accumulate(0, o.t, f.t, f.t, 3, 0, 64, 8, f.t, False)
+    qc.qc_majority_vote(o.t, 3, 0, o.t)
+    sync()
+    assert np.all(o.host() == 0xA5) and np.all(f.host() == 0xA5)
+
+
+def test_rejected_call_writes_nothing(qc):
+    o = Out(64)
+    f = out_f32(16)
+    with pytest.raises(qc.QcError) as e:
+        qc.qc_encode_uniform(f.t, None, 16, 64, 3, o.t, f.t, f.t)
+    assert e.value.status == qc.QC_ERR_UNSUPPORTED
+    with pytest.raises(qc.QcError) as e:
+        qc.qc_encode_uniform(f.raw.data_ptr() + 4, None, 16, 64, 8, o.t, f.t, f.t)
+    assert e.value.status == qc.QC_ERR_ALIGN
+    sync()
+    assert np.all(o.host() == 0xA5)
+
+
+def test_deterministic_and_stream_async(qc, ora):
+    """Two runs give identical bits; a call on a side stream is ordered by
+    that stream only."""
+    import torch
+
+    n, B = 1 << 20, 512
+    x = synth.host_laplace(n, 1e-4, seed=5)
+    a, na = run_qsgd(qc, x, None, B, 1234, 0)
+    b, nb_ = run_qsgd(qc, x, None, B, 1234, 0)
+    assert bits_equal(a.host(), b.host()) and bits_equal(na.f32(), nb_.f32())
+    s = torch.cuda.Stream()
+    xd = dev(x)
+    torch.cuda.synchronize()
+    words = Out(qc.payload_bytes(qc.QC_QSGD, n, B, 16))
+    norm = out_f32(qc.nbuckets(n, B))
+    with torch.cuda.stream(s):
+        qc.qc_encode_qsgd(xd, None, n, B, 16, 1234, 0, words.t, norm.t, stream=s)
+    s.synchronize()
+    assert bits_equal(words.host(), a.host())
