@@ -1,0 +1,376 @@
+"""Benchmark of the quantized-communication codec on one MI355X.
+
+One step is one pass of the whole codec hot path over one batch of
+synthetic input, every op at its full workload size:
+
+  uniform INT8 + error feedback, 65,536 fp32 (buckets of 4,096), and decode
+  rowwise FP8-E4M3 encode of 1,000,000 x 128 fp32 embedding rows, and decode
+  QSGD + error feedback, 1e9 fp32 (buckets of 512, Philox rounding), and decode
+  1-bit sign + error feedback, 2^28 bf16 (buckets of 4,096), and decode
+  majority vote over 16 sign payloads of 2^28 bits
+  dequantize-accumulate of 64 INT8 payloads of 2^26 (buckets of 2,048)
+    with the sum requantized to INT8 in the same pass
+
+Encoders run first and decoders later in the step, so a decoder never
+reads a payload that is still in the 256 MB last-level cache.  Inputs are
+generated on the GPU (seeded) before timing; the timed region only runs
+the kernels.
+
+Printed: one JSON line.  `value` is codec throughput in GB/s of logical
+input (fp32 bytes of each encoded/decoded tensor, bf16 bytes for the sign
+encoder's input, m*n*4 for the accumulation, packed bits for the vote)
+summed over the step and divided by the step time.  `ops` gives each op's
+time, its input GB/s and its algorithmic HBM GB/s against the 8 TB/s peak;
+`roofline` is that figure for the op with the largest time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+CSRC = os.path.join(ROOT, "embedding_communication_codecs_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_codec_suite.json")
+
+# workload sizes
+C1_N, C1_B = 65536, 4096
+C2_ROWS, C2_DIM = 1_000_000, 128
+C3_N, C3_B = 1_000_000_000, 512
+C4_N, C4_B, C4_M = 1 << 28, 4096, 16
+C5_M, C5_N, C5_B = 64, 1 << 26, 2048
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def op_bytes():
+    """(logical input bytes, algorithmic HBM bytes read+written) per op."""
+    nb1 = -(-C1_N // C1_B)
+    n2 = C2_ROWS * C2_DIM
+    nb3 = -(-C3_N // C3_B)
+    nb4 = -(-C4_N // C4_B)
+    nb5 = C5_N // C5_B
+    sign_pb = -(-C4_N // 32) * 4
+    return {
+        # x + ef read, ef written, codes + scale/zero written
+        "uniform_enc": (4 * C1_N, 4 * C1_N * 3 + C1_N + 8 * nb1),
+        "uniform_dec": (4 * C1_N, C1_N + 8 * nb1 + 4 * C1_N),
+        "fp8_enc": (4 * n2, 4 * n2 + n2 + 4 * C2_ROWS),
+        "fp8_dec": (4 * n2, n2 + 4 * C2_ROWS + 4 * n2),
+        "qsgd_enc": (4 * C3_N, 12 * C3_N + C3_N // 2 + 4 * nb3),
+        "qsgd_dec": (4 * C3_N, C3_N // 2 + 4 * nb3 + 4 * C3_N),
+        "sign_enc": (2 * C4_N, 2 * C4_N + 8 * C4_N + sign_pb + 4 * nb4),
+        "sign_vote": (C4_M * sign_pb, C4_M * sign_pb + sign_pb),
+        "sign_dec": (4 * C4_N, sign_pb + 4 * nb4 + 4 * C4_N),
+        "acc_requant": (4 * C5_M * C5_N, C5_M * (C5_N + 8 * nb5) + 4 * C5_N + C5_N + 8 * nb5),
+    }
+
+
+ORDER = ["uniform_enc", "qsgd_enc", "fp8_enc", "sign_enc", "acc_requant", "sign_vote", "qsgd_dec",
+         "fp8_dec", "sign_dec", "uniform_dec"]
+
+
+# ------------------------------------------------------------- GPU setup
+
+
+def setup(qc, synth, torch):
+    dev = torch.device("cuda")
+    st = {}
+    U8, F32 = torch.uint8, torch.float32
+
+    def empty(nbytes):
+        return torch.empty(nbytes, dtype=U8, device=dev)
+
+    # C1
+    st["c1_x"] = synth.device_normal(C1_N, 1e-3, 1001, dev)
+    st["c1_ef"] = torch.zeros(C1_N, dtype=F32, device=dev)
+    st["c1_codes"] = empty(qc.payload_bytes(qc.QC_UNIFORM, C1_N, C1_B, 8))
+    st["c1_scale"] = torch.empty(C1_N // C1_B, dtype=F32, device=dev)
+    st["c1_zero"] = torch.empty(C1_N // C1_B, dtype=F32, device=dev)
+    st["c1_out"] = torch.empty(C1_N, dtype=F32, device=dev)
+    # C2
+    st["c2_x"] = synth.device_embedding_rows(C2_ROWS, C2_DIM, 0.05, 0.001, 50.0, 2001, dev)
+    st["c2_codes"] = empty(qc.payload_bytes(qc.QC_FP8_ROWWISE, C2_ROWS * C2_DIM, C2_DIM, 8))
+    st["c2_scale"] = torch.empty(C2_ROWS, dtype=F32, device=dev)
+    st["c2_out"] = torch.empty(C2_ROWS * C2_DIM, dtype=F32, device=dev)
+    # C3
+    st["c3_x"] = synth.device_laplace(C3_N, 1e-4, 3001, dev)
+    st["c3_ef"] = torch.zeros(C3_N, dtype=F32, device=dev)
+    st["c3_words"] = empty(qc.payload_bytes(qc.QC_QSGD, C3_N, C3_B, 16))
+    st["c3_norm"] = torch.empty(-(-C3_N // C3_B), dtype=F32, device=dev)
+    st["c3_out"] = torch.empty(C3_N, dtype=F32, device=dev)
+    # C4
+    st["c4_x"] = synth.device_bf16_normal(C4_N, 1e-3, 4001, dev)
+    st["c4_ef"] = torch.zeros(C4_N, dtype=F32, device=dev)
+    pb4 = qc.payload_bytes(qc.QC_SIGN, C4_N, C4_B, 1)
+    st["c4_words"] = empty(pb4)
+    st["c4_scale"] = torch.empty(C4_N // C4_B, dtype=F32, device=dev)
+    st["c4_arena"] = synth.device_words(C4_M * pb4 // 4, 4100, dev)
+    st["c4_vote"] = empty(pb4)
+    st["c4_out"] = torch.empty(C4_N, dtype=F32, device=dev)
+    # C5: 64 workers' INT8 payloads, encoded from outlier gradients
+    pb5 = qc.payload_bytes(qc.QC_UNIFORM, C5_N, C5_B, 8)
+    nb5 = C5_N // C5_B
+    st["c5_arena"] = empty(C5_M * pb5)
+    st["c5_scale"] = torch.empty(C5_M * nb5, dtype=F32, device=dev)
+    st["c5_zero"] = torch.empty(C5_M * nb5, dtype=F32, device=dev)
+    for w in range(C5_M):
+        g = synth.device_outlier_grad(C5_N, 1e-3, 0.01, 100.0, 5000 + w, dev)
+        qc.qc_encode_uniform(g, None, C5_N, C5_B, 8, st["c5_arena"][w * pb5:(w + 1) * pb5],
+                             st["c5_scale"][w * nb5:(w + 1) * nb5], st["c5_zero"][w * nb5:(w + 1) * nb5])
+        del g
+    st["c5_acc"] = torch.empty(C5_N, dtype=F32, device=dev)
+    st["c5_rq"] = empty(pb5)
+    st["c5_rqs"] = torch.empty(nb5, dtype=F32, device=dev)
+    st["c5_rqz"] = torch.empty(nb5, dtype=F32, device=dev)
+    torch.cuda.synchronize()
+    return st
+
+
+def make_ops(qc, st):
+    s = st
+    return {
+        "uniform_enc": lambda: qc.qc_encode_uniform(s["c1_x"], s["c1_ef"], C1_N, C1_B, 8, s["c1_codes"],
+                                                    s["c1_scale"], s["c1_zero"]),
+        "uniform_dec": lambda: qc.qc_decode(qc.QC_UNIFORM, s["c1_codes"], s["c1_scale"], s["c1_zero"], C1_N,
+                                            C1_B, 8, s["c1_out"]),
+        "fp8_enc": lambda: qc.qc_encode_fp8_rowwise(s["c2_x"], C2_ROWS, C2_DIM, s["c2_codes"], s["c2_scale"]),
+        "fp8_dec": lambda: qc.qc_decode(qc.QC_FP8_ROWWISE, s["c2_codes"], s["c2_scale"], None,
+                                        C2_ROWS * C2_DIM, C2_DIM, 8, s["c2_out"]),
+        "qsgd_enc": lambda: qc.qc_encode_qsgd(s["c3_x"], s["c3_ef"], C3_N, C3_B, 16, 0x5153474400000001, 0,
+                                              s["c3_words"], s["c3_norm"]),
+        "qsgd_dec": lambda: qc.qc_decode(qc.QC_QSGD, s["c3_words"], s["c3_norm"], None, C3_N, C3_B, 16,
+                                         s["c3_out"]),
+        "sign_enc": lambda: qc.qc_encode_sign(s["c4_x"], qc.QC_BF16, s["c4_ef"], C4_N, C4_B, s["c4_words"],
+                                              s["c4_scale"]),
+        "sign_vote": lambda: qc.qc_majority_vote(s["c4_arena"], C4_M, C4_N, s["c4_vote"]),
+        "sign_dec": lambda: qc.qc_decode(qc.QC_SIGN, s["c4_words"], s["c4_scale"], None, C4_N, C4_B, 1,
+                                         s["c4_out"]),
+        "acc_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["c5_arena"], s["c5_scale"],
+                                                        s["c5_zero"], C5_M, C5_N, C5_B, 8, s["c5_acc"], False,
+                                                        s["c5_rq"], s["c5_rqs"], s["c5_rqz"]),
+    }
+
+
+# ----------------------------------------------------------- cpu baseline
+
+
+def cpu_baseline():
+    """The CPU oracle, single-threaded, on a bounded sample of each op."""
+    import numpy as np
+
+    import oracle as ora
+    from embedding_communication_codecs_amd import synth
+
+    ora.lib()
+    total_in, total_t = 0, 0.0
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    # uniform (whole workload: it is small)
+    g = synth.host_normal(C1_N, 1e-3, 1001)
+    ef = np.zeros(C1_N, np.float32)
+    (p, s, z), t = timed(lambda: ora.encode_uniform(g, ef, C1_B, 8))
+    _, t2 = timed(lambda: ora.decode_uniform(p, s, z, C1_N, C1_B, 8))
+    total_in += 8 * C1_N
+    total_t += t + t2
+    # fp8: the whole 1,000,000 x 128 workload
+    rows = C2_ROWS
+    x = synth.host_embedding_rows(rows, C2_DIM, 0.05, 0.001, 50.0, 2001)
+    (p, s), t = timed(lambda: ora.encode_fp8_rowwise(x, rows, C2_DIM))
+    _, t2 = timed(lambda: ora.decode_fp8_rowwise(p, s, rows, C2_DIM))
+    total_in += 8 * rows * C2_DIM
+    total_t += t + t2
+    # qsgd: 32M elements
+    n3 = 1 << 25
+    x = synth.host_laplace(n3, 1e-4, 3001)
+    ef = np.zeros(n3, np.float32)
+    (p, s), t = timed(lambda: ora.encode_qsgd(x, ef, C3_B, 0x5153474400000001, 0))
+    _, t2 = timed(lambda: ora.decode_qsgd(p, s, n3, C3_B))
+    total_in += 8 * n3
+    total_t += t + t2
+    # sign: 32M bf16, vote over 16 payloads of 32M bits, decode
+    n4 = 1 << 25
+    gb = synth.host_bf16_bits(synth.host_normal(n4, 1e-3, 4001))
+    ef = np.zeros(n4, np.float32)
+    (p, s), t = timed(lambda: ora.encode_sign(gb, ef, C4_B))
+    pb = ora.payload_bytes(ora.SIGN, n4, 1)
+    arena = np.concatenate([synth.host_words(pb // 4, 4100 + w).view(np.uint8) for w in range(C4_M)])
+    _, t2 = timed(lambda: ora.majority_vote(arena, C4_M, n4))
+    _, t3 = timed(lambda: ora.decode_sign(p, s, n4, C4_B))
+    total_in += 2 * n4 + C4_M * pb + 4 * n4
+    total_t += t + t2 + t3
+    # accumulate: 64 workers x 1M elements, then requantize
+    n5 = 1 << 20
+    parts, scs, zes = [], [], []
+    for w in range(C5_M):
+        pp, ss, zz = ora.encode_uniform(synth.host_outlier_grad(n5, 1e-3, 0.01, 100.0, 5000 + w), None, C5_B, 8)
+        parts.append(pp)
+        scs.append(ss)
+        zes.append(zz)
+    arena, sc, ze = np.concatenate(parts), np.concatenate(scs), np.concatenate(zes)
+    acc, t = timed(lambda: ora.dequant_accumulate(ora.UNIFORM, arena, sc, ze, C5_M, n5, C5_B, 8))
+    _, t2 = timed(lambda: ora.encode_uniform(acc, None, C5_B, 8))
+    total_in += 4 * C5_M * n5
+    total_t += t + t2
+    return {
+        "value": round(total_in / total_t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("every op of the step on a sample: uniform 65,536 (whole); fp8 1,000,000x128 (whole); "
+                   "qsgd 33,554,432; sign 33,554,432 bf16 + vote 16x33,554,432 bits + decode; "
+                   "accumulate 64x1,048,576 + requantize; single-threaded C oracle, same input-byte "
+                   f"accounting; {total_t:.1f} s of CPU time"),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+
+def load_traffic(kernel_op):
+    """HBM bytes per launch measured with rocprofv3 counters for this op,
+    if they were taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    e = t.get("ops", {}).get(kernel_op)
+    return None if e is None else e.get("hbm_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ops", default=",".join(ORDER), help="comma-separated subset of ops to run")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy each step (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the codec acts on one GPU's share of the payload and this "
+              "build has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import embedding_communication_codecs_amd as qc
+    from embedding_communication_codecs_amd import synth
+
+    qc.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    names = [o for o in ORDER if o in args.ops.split(",")]
+    print(f"[bench] generating inputs for {names}", file=sys.stderr, flush=True)
+    st = setup(qc, synth, torch)
+    ops = make_ops(qc, st)
+    if args.copy_calibration:
+        cal_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        cal_dst = torch.empty_like(cal_src)
+    sizes = op_bytes()
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for o in names:
+            ops[o]()
+        if args.copy_calibration:
+            cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = {o: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for o in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for o in names:
+            a, b = ev[o][k]
+            a.record(stream)
+            ops[o]()
+            b.record(stream)
+        if args.copy_calibration:
+            cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_op = {}
+    total_in = 0
+    for o in names:
+        ms = sum(a.elapsed_time(b) for a, b in ev[o]) / args.steps
+        inb, hbm = sizes[o]
+        total_in += inb
+        per_op[o] = {
+            "ms": round(ms, 4),
+            "input_GBps": round(inb / (ms * 1e-3) / 1e9, 1),
+            "hbm_GBps": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": hbm,
+        }
+    dom = max(names, key=lambda o: per_op[o]["ms"])
+    achieved = per_op[dom]["hbm_GBps"]
+    traffic = load_traffic(dom)
+    result = {
+        "metric": "codec GB/s (fp32 in, encode+EF / decode+accum) and % of MI355X HBM peak",
+        "value": round(total_in / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "codec_suite: " + ", ".join(names),
+            "uniform": f"{C1_N} fp32, bucket {C1_B}, INT8, EF",
+            "fp8_rowwise": f"{C2_ROWS}x{C2_DIM} fp32",
+            "qsgd": f"{C3_N} fp32, bucket {C3_B}, s=16, EF",
+            "sign": f"{C4_N} bf16, bucket {C4_B}, EF; vote M={C4_M}",
+            "accumulate": f"M={C5_M} x {C5_N} INT8, bucket {C5_B}, fused INT8 requant",
+        },
+        "hbm_frac_step": round(sum(sizes[o][1] for o in names) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "ops": per_op,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
