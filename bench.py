@@ -241,6 +241,39 @@ def cpu_baseline():
     }
 
 
+def calibrate(torch, reps=10):
+    """Achievable HBM rates of plain library kernels on 4 GiB buffers: a
+    copy (read + write), a fill (write only) and a max-reduction (read
+    only).  These are the practical ceilings the codec kernels are held to
+    beside the 8 TB/s nominal peak."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+
+    def avg_ms(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    nbytes = 4 * n
+    out = {
+        "copy_GBps": round(2 * nbytes / avg_ms(lambda: b.copy_(a)) / 1e6, 1),
+        "fill_GBps": round(nbytes / avg_ms(lambda: b.fill_(2.0)) / 1e6, 1),
+        "read_GBps": round(nbytes / avg_ms(lambda: a.amax()) / 1e6, 1),
+        "bytes": nbytes,
+    }
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -267,6 +300,8 @@ def main():
     ap.add_argument("--ops", default=",".join(ORDER), help="comma-separated subset of ops to run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy each step (counter calibration)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure plain copy/fill/read bandwidth and print it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -283,6 +318,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        print(json.dumps({"calibration": calibrate(torch)}))
+        return
     names = [o for o in ORDER if o in args.ops.split(",")]
     print(f"[bench] generating inputs for {names}", file=sys.stderr, flush=True)
     st = setup(qc, synth, torch)

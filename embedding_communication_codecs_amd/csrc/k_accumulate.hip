@@ -70,13 +70,178 @@ __device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s,
     }
 }
 
+// Loads of worker w's chunks and statistics for one bucket.
+template <class G, int F, bool FULL>
+__device__ __forceinline__ void load_worker(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+                                            const float* __restrict__ zero, int64_t pbytes, int64_t nb,
+                                            int64_t bk, int64_t base, int64_t n, int32_t w,
+                                            ChunkBits<F> (&c)[G::K], float& s, float& z) {
+    const uint8_t* pw = codes + (int64_t)w * pbytes;
+    s = scale[(int64_t)w * nb + bk];
+    z = 0.0f;
+    if constexpr (F == A_U8 || F == A_U4) z = zero[(int64_t)w * nb + bk];
+#pragma unroll
+    for (int k = 0; k < G::K; ++k) {
+        const int64_t i = base + (int64_t)k * G::LPB * 16;
+        if (FULL || i < n) c[k] = load_chunk<F>(pw, i);
+        else c[k].v = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <class G, int F, int RQBITS, bool RQ, bool FULL>
+__device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+                                           const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb,
+                                           int64_t pbytes, float* __restrict__ acc, int32_t accumulate,
+                                           uint8_t* __restrict__ rq_codes, int64_t rq_pbytes,
+                                           float* __restrict__ rq_scale, float* __restrict__ rq_zero,
+                                           int64_t bk, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB, UW = 4;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+
+    float a[K][16];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 16;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[k][j] = 0.0f;
+        if (accumulate) {
+            if (FULL || i + 16 <= n) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 t = ld_f4(acc + i + 4 * q);
+                    a[k][4 * q] = t.x; a[k][4 * q + 1] = t.y;
+                    a[k][4 * q + 2] = t.z; a[k][4 * q + 3] = t.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (i + j < n) a[k][j] = acc[i + j];
+            }
+        }
+    }
+
+    // Software pipeline over groups of UW workers: the loads of group g+1
+    // are in flight while group g's terms are added (in worker order).  The
+    // prefetch clamps the worker index to m-1, so it needs no branch; the
+    // repeated loads of the last group are never added.
+    ChunkBits<F> cur[UW][K];
+    float cs[UW], cz[UW];
+#pragma unroll
+    for (int u = 0; u < UW; ++u)
+        load_worker<G, F, FULL>(codes, scale, zero, pbytes, nb, bk, base, n, u < m ? u : m - 1, cur[u],
+                                cs[u], cz[u]);
+    for (int32_t w0 = 0; w0 < m; w0 += UW) {
+        ChunkBits<F> nxt[UW][K];
+        float ns[UW], nz[UW];
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+            const int32_t w = w0 + UW + u < m ? w0 + UW + u : m - 1;
+            load_worker<G, F, FULL>(codes, scale, zero, pbytes, nb, bk, base, n, w, nxt[u], ns[u], nz[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+            if (w0 + u >= m) break;
+            if constexpr (F == A_QSGD) cz[u] = cs[u] / 7.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(cur[u][k], j, cs[u], cz[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) cur[u][k] = nxt[u][k];
+            cs[u] = ns[u];
+            cz[u] = nz[u];
+        }
+    }
+
+    // acc is written with plain stores: a lane's 16 sums are 64 contiguous
+    // bytes, so one store instruction covers every fourth 16-byte piece of
+    // a span, and L2 has to merge the four instructions' pieces into whole
+    // lines before they go to HBM (streaming stores would not be merged).
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 16;
+        if (FULL || i + 16 <= n) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(acc + i + 4 * q) =
+                    f32x4{a[k][4 * q], a[k][4 * q + 1], a[k][4 * q + 2], a[k][4 * q + 3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (i + j < n) acc[i + j] = a[k][j];
+        }
+    }
+
+    if constexpr (RQ) {
+        // requantize the bucket's sums: the uniform rule with no feedback
+        constexpr uint32_t L = (1u << RQBITS) - 1u;
+        float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (FULL || base + (int64_t)k * LPB * 16 + j < n) {
+                    mn = fminf(mn, a[k][j]);
+                    mx = fmaxf(mx, a[k][j]);
+                }
+        mn = group_min<LPB>(mn);
+        mx = group_max<LPB>(mx);
+        if constexpr (G::W > 1) {
+            mn = block_min<G::W>(mn, lds);
+            mx = block_max<G::W>(mx, lds);
+        }
+        mn = mn + 0.0f;
+        mx = mx + 0.0f;
+        const float sc = (mx - mn) / (float)L;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t i = base + (int64_t)k * LPB * 16;
+            uint32_t q[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                uint32_t cq = 0;
+                if (sc != 0.0f) {
+                    const float t = (a[k][j] - mn) / sc;
+                    cq = (uint32_t)fminf(fmaxf(__builtin_rintf(t), 0.0f), (float)L);
+                }
+                q[j] = (FULL || i + j < n) ? cq : 0u;
+            }
+            if constexpr (RQBITS == 8) {
+                u32x4 o;
+                o.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+                o.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+                o.z = q[8] | (q[9] << 8) | (q[10] << 16) | (q[11] << 24);
+                o.w = q[12] | (q[13] << 8) | (q[14] << 16) | (q[15] << 24);
+                if (FULL || i < rq_pbytes) st_u4(rq_codes + i, o);
+            } else {
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    lo |= q[j] << (4 * j);
+                    hi |= q[8 + j] << (4 * j);
+                }
+                if (FULL || i / 2 < rq_pbytes) {
+                    st_u32(rq_codes + i / 2, lo);
+                    st_u32(rq_codes + i / 2 + 4, hi);
+                }
+            }
+        }
+        if (bucket_leader<G>()) {
+            rq_scale[bk] = sc;
+            rq_zero[bk] = mn;
+        }
+    }
+}
+
 template <class G, int F, int RQBITS, bool RQ>
 __global__ void __launch_bounds__(G::THREADS)
 k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
               const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb, int64_t pbytes,
               float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,
               int64_t rq_pbytes, float* __restrict__ rq_scale, float* __restrict__ rq_zero) {
-    constexpr int K = G::K, LPB = G::LPB, UW = 4;
     __shared__ float lds[G::W];
 
     // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs,
@@ -87,146 +252,18 @@ k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale
     if (vblock * G::BPB >= nb) return;  // spare blocks when gridDim.x % 8 != 0
 
     const int64_t first = G::W > 1 ? vblock
-                                   : vblock * G::BPB + wave_id() * G::GROUPS + lane_id() / LPB;
-    for (int64_t bk = first; bk < nb; bk += (int64_t)per_xcd * 8 * G::BPB) {
+                                   : vblock * G::BPB + wave_id() * G::GROUPS + lane_id() / G::LPB;
+    for (int64_t bk = first; bk < nb; bk += per_xcd * 8 * G::BPB) {
         int64_t bks = bk;
-        if constexpr (LPB == WAVE) bks = __builtin_amdgcn_readfirstlane((int)bk);
-        const int64_t base = bks * (int64_t)G::B + lane_offset<G>();
-
-        float a[K][16];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int64_t i = base + (int64_t)k * LPB * 16;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) a[k][j] = 0.0f;
-            if (accumulate) {
-                if (i + 16 <= n) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 t = ld_f4(acc + i + 4 * q);
-                        a[k][4 * q] = t.x; a[k][4 * q + 1] = t.y;
-                        a[k][4 * q + 2] = t.z; a[k][4 * q + 3] = t.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (i + j < n) a[k][j] = acc[i + j];
-                }
-            }
-        }
-
-        int32_t w0 = 0;
-        for (; w0 + UW <= m; w0 += UW) {
-            ChunkBits<F> c[UW][K];
-            float s[UW], z[UW];
-#pragma unroll
-            for (int u = 0; u < UW; ++u) {
-                const uint8_t* pw = codes + (int64_t)(w0 + u) * pbytes;
-                s[u] = scale[(int64_t)(w0 + u) * nb + bks];
-                if constexpr (F == A_U8 || F == A_U4) z[u] = zero[(int64_t)(w0 + u) * nb + bks];
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const int64_t i = base + (int64_t)k * LPB * 16;
-                    c[u][k] = i < n ? load_chunk<F>(pw, i) : ChunkBits<F>{u32x4{0u, 0u, 0u, 0u}};
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UW; ++u) {
-                if constexpr (F == A_QSGD) z[u] = s[u] / 7.0f;
-#pragma unroll
-                for (int k = 0; k < K; ++k)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(c[u][k], j, s[u], z[u]);
-            }
-        }
-        for (; w0 < m; ++w0) {
-            const uint8_t* pw = codes + (int64_t)w0 * pbytes;
-            const float s = scale[(int64_t)w0 * nb + bks];
-            float z = 0.0f;
-            if constexpr (F == A_U8 || F == A_U4) z = zero[(int64_t)w0 * nb + bks];
-            if constexpr (F == A_QSGD) z = s / 7.0f;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t i = base + (int64_t)k * LPB * 16;
-                const ChunkBits<F> c = i < n ? load_chunk<F>(pw, i) : ChunkBits<F>{u32x4{0u, 0u, 0u, 0u}};
-#pragma unroll
-                for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(c, j, s, z);
-            }
-        }
-
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int64_t i = base + (int64_t)k * LPB * 16;
-            if (i + 16 <= n) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    st_f4(acc + i + 4 * q, f32x4{a[k][4 * q], a[k][4 * q + 1], a[k][4 * q + 2], a[k][4 * q + 3]});
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (i + j < n) acc[i + j] = a[k][j];
-            }
-        }
-
-        if constexpr (RQ) {
-            // requantize the bucket's sums: the uniform rule with no feedback
-            constexpr uint32_t L = (1u << RQBITS) - 1u;
-            float mn = __builtin_inff(), mx = -__builtin_inff();
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    if (base + (int64_t)k * LPB * 16 + j < n) {
-                        mn = fminf(mn, a[k][j]);
-                        mx = fmaxf(mx, a[k][j]);
-                    }
-            mn = group_min<LPB>(mn);
-            mx = group_max<LPB>(mx);
-            if constexpr (G::W > 1) {
-                mn = block_min<G::W>(mn, lds);
-                mx = block_max<G::W>(mx, lds);
-            }
-            mn = mn + 0.0f;
-            mx = mx + 0.0f;
-            const float sc = (mx - mn) / (float)L;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int64_t i = base + (int64_t)k * LPB * 16;
-                uint32_t q[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    uint32_t cq = 0;
-                    if (sc != 0.0f) {
-                        const float t = (a[k][j] - mn) / sc;
-                        cq = (uint32_t)fminf(fmaxf(__builtin_rintf(t), 0.0f), (float)L);
-                    }
-                    q[j] = (i + j < n) ? cq : 0u;
-                }
-                if constexpr (RQBITS == 8) {
-                    u32x4 o;
-                    o.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-                    o.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-                    o.z = q[8] | (q[9] << 8) | (q[10] << 16) | (q[11] << 24);
-                    o.w = q[12] | (q[13] << 8) | (q[14] << 16) | (q[15] << 24);
-                    if (i < rq_pbytes) st_u4(rq_codes + i, o);
-                } else {
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        lo |= q[j] << (4 * j);
-                        hi |= q[8 + j] << (4 * j);
-                    }
-                    if (i / 2 < rq_pbytes) {
-                        st_u32(rq_codes + i / 2, lo);
-                        st_u32(rq_codes + i / 2 + 4, hi);
-                    }
-                }
-            }
-            if (bucket_leader<G>()) {
-                rq_scale[bk] = sc;
-                rq_zero[bk] = mn;
-            }
-        }
+        // a bucket spanning whole waves has a wave-uniform index: keep it in
+        // scalar registers so per-worker statistics come through the scalar cache
+        if constexpr (G::LPB == WAVE) bks = __builtin_amdgcn_readfirstlane((int)bk);
+        if ((bks + 1) * (int64_t)G::B <= n)
+            acc_bucket<G, F, RQBITS, RQ, true>(codes, scale, zero, m, n, nb, pbytes, acc, accumulate,
+                                               rq_codes, rq_pbytes, rq_scale, rq_zero, bks, lds);
+        else
+            acc_bucket<G, F, RQBITS, RQ, false>(codes, scale, zero, m, n, nb, pbytes, acc, accumulate,
+                                                rq_codes, rq_pbytes, rq_scale, rq_zero, bks, lds);
     }
 }
 

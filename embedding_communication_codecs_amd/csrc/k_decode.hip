@@ -47,6 +47,46 @@ __device__ __forceinline__ float chunk_value(uint32_t w, int j, float s, float z
     }
 }
 
+template <int F, bool POW2, int U, bool FULL>
+__device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+                                            const float* __restrict__ zero, int64_t n, int64_t nchunks,
+                                            int64_t group, int gshift, float* __restrict__ out, int64_t t0) {
+    uint32_t w[U];
+    float s[U], z[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = t0 + u * 256 + threadIdx.x;
+        w[u] = 0u;
+        s[u] = 0.0f;
+        z[u] = 0.0f;
+        if (FULL || c < nchunks) {
+            const int64_t bk = POW2 ? ((c << 2) >> gshift) : ((c << 2) / group);
+            w[u] = chunk_word<F>(codes, c);
+            s[u] = scale[bk];
+            if constexpr (F == F_U8 || F == F_U4) z[u] = zero[bk];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t c = t0 + u * 256 + threadIdx.x;
+        if (!FULL && c >= nchunks) continue;
+        if constexpr (F == F_QSGD) z[u] = s[u] / 7.0f;
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = chunk_value<F>(w[u], j, s[u], z[u]);
+        const int64_t i = c << 2;
+        if (FULL || i + 4 <= n) {
+            st_f4(out + i, f32x4{o[0], o[1], o[2], o[3]});
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i + j < n) out[i + j] = o[j];
+        }
+    }
+}
+
+// A tile is 256*U chunks.  Tiles wholly inside n (all but at most the last)
+// take the branch-free path, so a thread's U loads issue back to back.
 template <int F, bool POW2, int U>
 __global__ void __launch_bounds__(256)
 k_decode(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
@@ -54,38 +94,10 @@ k_decode(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
     const int64_t nchunks = (n + 3) >> 2;
     constexpr int64_t TILE = 256 * U;
     for (int64_t t0 = (int64_t)blockIdx.x * TILE; t0 < nchunks; t0 += (int64_t)gridDim.x * TILE) {
-        uint32_t w[U];
-        float s[U], z[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = t0 + u * 256 + threadIdx.x;
-            w[u] = 0u;
-            s[u] = 0.0f;
-            z[u] = 0.0f;
-            if (c < nchunks) {
-                const int64_t bk = POW2 ? ((c << 2) >> gshift) : ((c << 2) / group);
-                w[u] = chunk_word<F>(codes, c);
-                s[u] = scale[bk];
-                if constexpr (F == F_U8 || F == F_U4) z[u] = zero[bk];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = t0 + u * 256 + threadIdx.x;
-            if (c >= nchunks) continue;
-            if constexpr (F == F_QSGD) z[u] = s[u] / 7.0f;
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = chunk_value<F>(w[u], j, s[u], z[u]);
-            const int64_t i = c << 2;
-            if (i + 4 <= n) {
-                st_f4(out + i, f32x4{o[0], o[1], o[2], o[3]});
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (i + j < n) out[i + j] = o[j];
-            }
-        }
+        if ((t0 + TILE) * 4 <= n)
+            decode_tile<F, POW2, U, true>(codes, scale, zero, n, nchunks, group, gshift, out, t0);
+        else
+            decode_tile<F, POW2, U, false>(codes, scale, zero, n, nchunks, group, gshift, out, t0);
     }
 }
 

@@ -8,18 +8,23 @@
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
 
+#include <type_traits>
+
 namespace qc {
 namespace {
 
 // --------------------------------------------------------------- loading
 // Load chunk k (E = 4 fp32 elements at index i) as v = ef + x.  Elements at
-// or past n read as 0 and are masked by the caller.
-template <bool FULL>
+// or past n read as 0 and are masked by the caller.  Error feedback is a
+// template parameter so that a full bucket's loads are straight-line code
+// the compiler can issue back to back (a runtime branch between them makes
+// it drain each load before the next).
+template <bool FULL, bool EF>
 __device__ __forceinline__ void load4(const float* __restrict__ x, const float* __restrict__ ef,
                                       int64_t i, int64_t n, float (&v)[4]) {
     if (FULL || i + 4 <= n) {
         f32x4 g = ld_f4(x + i);
-        if (ef) g = ld_f4(ef + i) + g;
+        if constexpr (EF) g = ld_f4(ef + i) + g;
         v[0] = g.x; v[1] = g.y; v[2] = g.z; v[3] = g.w;
     } else {
 #pragma unroll
@@ -27,7 +32,7 @@ __device__ __forceinline__ void load4(const float* __restrict__ x, const float* 
             float g = 0.0f;
             if (i + j < n) {
                 g = x[i + j];
-                if (ef) g = ef[i + j] + g;
+                if constexpr (EF) g = ef[i + j] + g;
             }
             v[j] = g;
         }
@@ -50,7 +55,7 @@ __device__ __forceinline__ void store_ef4(float* __restrict__ ef, int64_t i, int
 // scale = (max - min) / (2^BITS - 1); code = rint((v - min) / scale);
 // DQ = code*scale + min; ef = v - DQ.
 
-template <class G, int BITS, bool FULL>
+template <class G, int BITS, bool EF, bool FULL>
 __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, float* __restrict__ ef,
                                                int64_t n, int64_t bk, uint8_t* __restrict__ codes,
                                                int64_t pbytes, float* __restrict__ scale,
@@ -61,7 +66,7 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
 
     float v[K][4];
 #pragma unroll
-    for (int k = 0; k < K; ++k) load4<FULL>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
 
     float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
@@ -109,7 +114,7 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
             const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
             if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(codes + i / 2, half | (other << 16));
         }
-        if (ef) store_ef4<FULL>(ef, i, n, e);
+        if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
     }
     if (bucket_leader<G>()) {
         scale[bk] = sc;
@@ -117,7 +122,7 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
     }
 }
 
-template <class G, int BITS>
+template <class G, int BITS, bool EF>
 __global__ void __launch_bounds__(G::THREADS)
 k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
               uint8_t* __restrict__ codes, int64_t pbytes, float* __restrict__ scale,
@@ -125,9 +130,9 @@ k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, in
     __shared__ float lds[G::W];
     for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
         if ((bk + 1) * (int64_t)G::B <= n)
-            uniform_bucket<G, BITS, true>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+            uniform_bucket<G, BITS, EF, true>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
         else
-            uniform_bucket<G, BITS, false>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+            uniform_bucket<G, BITS, EF, false>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
     }
 }
 
@@ -135,7 +140,7 @@ k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, in
 // norm = sqrt(pairwise sum of v^2); d = norm/7; level = floor(|v|/d) + Bernoulli(frac)
 // drawn from Philox4x32-10 word g%4 of counter g/4 (g = global index).
 
-template <class G, bool FULL>
+template <class G, bool EF, bool FULL>
 __device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* __restrict__ ef,
                                             int64_t n, int64_t bk, uint32_t k0, uint32_t k1,
                                             uint64_t elem_offset, uint8_t* __restrict__ words,
@@ -145,7 +150,7 @@ __device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* 
 
     float v[K][4];
 #pragma unroll
-    for (int k = 0; k < K; ++k) load4<FULL>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
 
     float s[K];
 #pragma unroll
@@ -188,12 +193,12 @@ __device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* 
         const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
         const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
         if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(words + i / 2, half | (other << 16));
-        if (ef) store_ef4<FULL>(ef, i, n, e);
+        if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
     }
     if (bucket_leader<G>()) norm[bk] = nrm;
 }
 
-template <class G>
+template <class G, bool EF>
 __global__ void __launch_bounds__(G::THREADS)
 k_enc_qsgd(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0,
            uint32_t k1, uint64_t elem_offset, uint8_t* __restrict__ words, int64_t pbytes,
@@ -201,9 +206,9 @@ k_enc_qsgd(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
     __shared__ float lds[G::W];
     for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
         if ((bk + 1) * (int64_t)G::B <= n)
-            qsgd_bucket<G, true>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
+            qsgd_bucket<G, EF, true>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
         else
-            qsgd_bucket<G, false>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
+            qsgd_bucket<G, EF, false>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
     }
 }
 
@@ -211,7 +216,7 @@ k_enc_qsgd(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
 // scale = (pairwise sum of |v|) / count; bit = v < 0; DQ = bit ? -scale : scale.
 // fp32 input: chunks of 4 elements; bf16 input: chunks of 8 (16 bytes).
 
-template <class G, bool BF16, bool FULL>
+template <class G, bool BF16, bool EF, bool FULL>
 __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* __restrict__ ef,
                                             int64_t n, int64_t bk, int64_t nb,
                                             uint8_t* __restrict__ words, int64_t pbytes,
@@ -233,7 +238,7 @@ __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* 
                     v[k][2 * h] = bf16_to_f32(ww[h] & 0xFFFFu);
                     v[k][2 * h + 1] = bf16_to_f32(ww[h] >> 16);
                 }
-                if (ef) {
+                if constexpr (EF) {
                     const f32x4 e0 = ld_f4(ef + i), e1 = ld_f4(ef + i + 4);
                     const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
@@ -245,7 +250,7 @@ __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* 
                     float g = 0.0f;
                     if (i + j < n) {
                         g = bf16_to_f32(x[i + j]);
-                        if (ef) g = ef[i + j] + g;
+                        if constexpr (EF) g = ef[i + j] + g;
                     }
                     v[k][j] = g;
                 }
@@ -253,7 +258,7 @@ __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* 
         } else {
             const float* x = static_cast<const float*>(xv);
             float t[4];
-            load4<FULL>(x, ef, i, n, t);
+            load4<FULL, EF>(x, ef, i, n, t);
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[k][j] = t[j];
         }
@@ -287,7 +292,7 @@ __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* 
         }
         const uint32_t word = group_or<LPW>(bits << (E * (lane_id() % LPW)));
         if (lane_id() % LPW == 0 && i / 8 < pbytes) st_u32(words + i / 8, word);
-        if (ef) {
+        if constexpr (EF) {
             if constexpr (E == 8) {
                 if (FULL || i + 8 <= n) {
                     st_f4(ef + i, f32x4{e[0], e[1], e[2], e[3]});
@@ -312,7 +317,7 @@ __device__ __forceinline__ void sign_bucket(const void* __restrict__ xv, float* 
     }
 }
 
-template <class G, bool BF16>
+template <class G, bool BF16, bool EF>
 __global__ void __launch_bounds__(G::THREADS)
 k_enc_sign(const void* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
            uint8_t* __restrict__ words, int64_t pbytes, float* __restrict__ scale) {
@@ -320,9 +325,9 @@ k_enc_sign(const void* __restrict__ x, float* __restrict__ ef, int64_t n, int64_
     for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
         // masked elements load as +0: v < 0 is false, so their bits are 0
         if ((bk + 1) * (int64_t)G::B <= n)
-            sign_bucket<G, BF16, true>(x, ef, n, bk, nb, words, pbytes, scale, lds);
+            sign_bucket<G, BF16, EF, true>(x, ef, n, bk, nb, words, pbytes, scale, lds);
         else
-            sign_bucket<G, BF16, false>(x, ef, n, bk, nb, words, pbytes, scale, lds);
+            sign_bucket<G, BF16, EF, false>(x, ef, n, bk, nb, words, pbytes, scale, lds);
     }
 }
 
@@ -355,6 +360,13 @@ hipError_t dispatch_bucket(int32_t bucket, F&& f) {
 
 }  // namespace
 
+// Calls f(std::true_type) or f(std::false_type): each kernel is compiled
+// once with and once without error feedback.
+template <class F>
+hipError_t with_flag(bool flag, F&& f) {
+    return flag ? f(std::true_type{}) : f(std::false_type{});
+}
+
 hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
                                  void* codes, int64_t payload_bytes, float* scale, float* zero,
                                  hipStream_t stream) {
@@ -362,13 +374,16 @@ hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t b
     return dispatch_bucket<4>(bucket, [&](auto g) {
         using G = decltype(g);
         const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
-        if (bits == 8)
-            hipLaunchKernelGGL((k_enc_uniform<G, 8>), grid, block, 0, stream, x, ef, n, nb,
-                               (uint8_t*)codes, payload_bytes, scale, zero);
-        else
-            hipLaunchKernelGGL((k_enc_uniform<G, 4>), grid, block, 0, stream, x, ef, n, nb,
-                               (uint8_t*)codes, payload_bytes, scale, zero);
-        return hipGetLastError();
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            if (bits == 8)
+                hipLaunchKernelGGL((k_enc_uniform<G, 8, EF>), grid, block, 0, stream, x, ef, n, nb,
+                                   (uint8_t*)codes, payload_bytes, scale, zero);
+            else
+                hipLaunchKernelGGL((k_enc_uniform<G, 4, EF>), grid, block, 0, stream, x, ef, n, nb,
+                                   (uint8_t*)codes, payload_bytes, scale, zero);
+            return hipGetLastError();
+        });
     });
 }
 
@@ -379,9 +394,12 @@ hipError_t launch_encode_qsgd(const float* x, float* ef, int64_t n, int32_t buck
     return dispatch_bucket<4>(bucket, [&](auto g) {
         using G = decltype(g);
         const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
-        hipLaunchKernelGGL((k_enc_qsgd<G>), grid, block, 0, stream, x, ef, n, nb, (uint32_t)seed,
-                           (uint32_t)(seed >> 32), elem_offset, (uint8_t*)words, payload_bytes, norm);
-        return hipGetLastError();
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            hipLaunchKernelGGL((k_enc_qsgd<G, EF>), grid, block, 0, stream, x, ef, n, nb, (uint32_t)seed,
+                               (uint32_t)(seed >> 32), elem_offset, (uint8_t*)words, payload_bytes, norm);
+            return hipGetLastError();
+        });
     });
 }
 
@@ -389,21 +407,19 @@ hipError_t launch_encode_sign(const void* x, bool bf16, float* ef, int64_t n, in
                               uint32_t* words, int64_t payload_bytes, float* scale,
                               hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
-    if (bf16)
-        return dispatch_bucket<8>(bucket, [&](auto g) {
-            using G = decltype(g);
-            const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
-            hipLaunchKernelGGL((k_enc_sign<G, true>), grid, block, 0, stream, x, ef, n, nb,
+    auto body = [&](auto g, auto is_bf16) {
+        using G = decltype(g);
+        constexpr bool BF16 = decltype(is_bf16)::value;
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            hipLaunchKernelGGL((k_enc_sign<G, BF16, EF>), grid, block, 0, stream, x, ef, n, nb,
                                (uint8_t*)words, payload_bytes, scale);
             return hipGetLastError();
         });
-    return dispatch_bucket<4>(bucket, [&](auto g) {
-        using G = decltype(g);
-        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
-        hipLaunchKernelGGL((k_enc_sign<G, false>), grid, block, 0, stream, x, ef, n, nb,
-                           (uint8_t*)words, payload_bytes, scale);
-        return hipGetLastError();
-    });
+    };
+    if (bf16) return dispatch_bucket<8>(bucket, [&](auto g) { return body(g, std::true_type{}); });
+    return dispatch_bucket<4>(bucket, [&](auto g) { return body(g, std::false_type{}); });
 }
 
 }  // namespace qc

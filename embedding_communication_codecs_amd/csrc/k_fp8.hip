@@ -36,37 +36,48 @@ __device__ __forceinline__ void fp8_zero_tail(uint8_t* codes, int64_t used, int6
     for (int64_t b = used; b < pbytes; b += 4) st_u32(codes + b, 0u);
 }
 
+template <int LPR, int RG, bool FULL>
+__device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t rows, uint8_t* __restrict__ codes,
+                                         int64_t pbytes, float* __restrict__ scale, int64_t r0) {
+    constexpr int DIM = LPR * 4;
+    constexpr int RPG = WAVE / LPR;  // rows per load instruction
+    const int l = lane_id() % LPR;
+    const int rsub = lane_id() / LPR;
+    f32x4 v[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int64_t row = r0 + g * RPG + rsub;
+        v[g] = (FULL || row < rows) ? ld_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int64_t row = r0 + g * RPG + rsub;
+        const float amax = group_max<LPR>(amax4(v[g]));
+        const float sc = amax / 448.0f;
+        const uint32_t word = fp8_pack4(v[g], sc);
+        if (FULL || row < rows) {
+            st_u32(codes + row * DIM + l * 4, word);
+            if (l == 0) {
+                scale[row] = sc;
+                if (row == rows - 1) fp8_zero_tail(codes, rows * DIM, pbytes);
+            }
+        }
+    }
+}
+
+// Wave w of the grid handles RPW = RG * 64/LPR consecutive rows per
+// iteration; groups of rows wholly inside `rows` take the branch-free path.
 template <int LPR, int RG>
 __global__ void __launch_bounds__(256)
 k_enc_fp8_pow2(const float* __restrict__ x, int64_t rows, uint8_t* __restrict__ codes,
                int64_t pbytes, float* __restrict__ scale) {
-    constexpr int DIM = LPR * 4;
-    constexpr int RPG = WAVE / LPR;  // rows per load instruction
-    constexpr int RPW = RPG * RG;    // rows per wave per iteration
-    const int l = lane_id() % LPR;
-    const int rsub = lane_id() / LPR;
+    constexpr int RPW = (WAVE / LPR) * RG;
     const int64_t wstride = (int64_t)gridDim.x * 4;
     for (int64_t r0 = ((int64_t)blockIdx.x * 4 + wave_id()) * RPW; r0 < rows; r0 += wstride * RPW) {
-        f32x4 v[RG];
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int64_t row = r0 + g * RPG + rsub;
-            v[g] = row < rows ? ld_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int64_t row = r0 + g * RPG + rsub;
-            const float amax = group_max<LPR>(amax4(v[g]));
-            const float sc = amax / 448.0f;
-            const uint32_t word = fp8_pack4(v[g], sc);
-            if (row < rows) {
-                st_u32(codes + row * DIM + l * 4, word);
-                if (l == 0) {
-                    scale[row] = sc;
-                    if (row == rows - 1) fp8_zero_tail(codes, rows * DIM, pbytes);
-                }
-            }
-        }
+        if (r0 + RPW <= rows)
+            fp8_rows<LPR, RG, true>(x, rows, codes, pbytes, scale, r0);
+        else
+            fp8_rows<LPR, RG, false>(x, rows, codes, pbytes, scale, r0);
     }
 }
 

@@ -4,7 +4,7 @@
 // the HIP runtime, so a rejected call enqueues nothing and writes nothing,
 // and the validation can be exercised on a machine without a GPU.  Valid
 // calls hand over to the launchers in the kernel sources.
-#include "../../include/qc.h"
+#include "qc.h"
 
 #include <hip/hip_runtime.h>
 
