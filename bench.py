@@ -197,16 +197,16 @@ def cpu_baseline():
     _, t2 = timed(lambda: ora.decode_fp8_rowwise(p, s, rows, C2_DIM))
     total_in += 8 * rows * C2_DIM
     total_t += t + t2
-    # qsgd: 32M elements
-    n3 = 1 << 25
+    # qsgd: 128M elements
+    n3 = 1 << 27
     x = synth.host_laplace(n3, 1e-4, 3001)
     ef = np.zeros(n3, np.float32)
     (p, s), t = timed(lambda: ora.encode_qsgd(x, ef, C3_B, 0x5153474400000001, 0))
     _, t2 = timed(lambda: ora.decode_qsgd(p, s, n3, C3_B))
     total_in += 8 * n3
     total_t += t + t2
-    # sign: 32M bf16, vote over 16 payloads of 32M bits, decode
-    n4 = 1 << 25
+    # sign: 128M bf16, vote over 16 payloads of 128M bits, decode
+    n4 = 1 << 27
     gb = synth.host_bf16_bits(synth.host_normal(n4, 1e-3, 4001))
     ef = np.zeros(n4, np.float32)
     (p, s), t = timed(lambda: ora.encode_sign(gb, ef, C4_B))
@@ -216,8 +216,8 @@ def cpu_baseline():
     _, t3 = timed(lambda: ora.decode_sign(p, s, n4, C4_B))
     total_in += 2 * n4 + C4_M * pb + 4 * n4
     total_t += t + t2 + t3
-    # accumulate: 64 workers x 1M elements, then requantize
-    n5 = 1 << 20
+    # accumulate: 64 workers x 4M elements, then requantize
+    n5 = 1 << 22
     parts, scs, zes = [], [], []
     for w in range(C5_M):
         pp, ss, zz = ora.encode_uniform(synth.host_outlier_grad(n5, 1e-3, 0.01, 100.0, 5000 + w), None, C5_B, 8)
@@ -235,8 +235,8 @@ def cpu_baseline():
         "cores": 1,
         "kind": "oracle",
         "sample": ("every op of the step on a sample: uniform 65,536 (whole); fp8 1,000,000x128 (whole); "
-                   "qsgd 33,554,432; sign 33,554,432 bf16 + vote 16x33,554,432 bits + decode; "
-                   "accumulate 64x1,048,576 + requantize; single-threaded C oracle, same input-byte "
+                   "qsgd 134,217,728; sign 134,217,728 bf16 + vote 16x134,217,728 bits + decode; "
+                   "accumulate 64x4,194,304 + requantize; single-threaded C oracle, same input-byte "
                    f"accounting; {total_t:.1f} s of CPU time"),
     }
 

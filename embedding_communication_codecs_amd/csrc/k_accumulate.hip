@@ -12,9 +12,10 @@
 // to reduce min/max over the bucket without a second pass over acc.
 //
 // The per-(worker, bucket) scale and zero are uniform across a wave when a
-// bucket spans whole waves, and are then read through the scalar cache.
-// Blocks are mapped to buckets XCD by XCD (consecutive buckets on one XCD),
-// so neighbouring buckets' statistics share that XCD's L2 lines.
+// bucket spans whole waves; one vector load brings 64 workers' values into
+// a register across the wave (see Stats).  Blocks are mapped to buckets XCD
+// by XCD (consecutive buckets on one XCD), so neighbouring buckets'
+// statistics share that XCD's L2 lines.
 //
 // Bounds: a chunk starting below n reads its codes inside the 16-byte
 // padded payload (see the payload rules in qc.h).
@@ -37,12 +38,12 @@ template <int F>
 __device__ __forceinline__ ChunkBits<F> load_chunk(const uint8_t* __restrict__ p, int64_t i) {
     ChunkBits<F> r;
     if constexpr (F == A_U8 || F == A_FP8) {
-        r.v = ld_u4(p + i);
+        r.v = ld_stream_u4(p + i);
     } else if constexpr (F == A_U4 || F == A_QSGD) {
-        const u32x2 h = *reinterpret_cast<const u32x2*>(p + i / 2);
+        const u32x2 h = ld_stream_u2(p + i / 2);
         r.v = u32x4{h.x, h.y, 0u, 0u};
     } else {
-        const uint32_t h = *reinterpret_cast<const uint16_t*>(p + i / 8);
+        const uint32_t h = ld_stream_u16(p + i / 8);
         r.v = u32x4{h, 0u, 0u, 0u};
     }
     return r;
@@ -70,16 +71,53 @@ __device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s,
     }
 }
 
-// Loads of worker w's chunks and statistics for one bucket.
+constexpr bool has_zero(int F) { return F == A_U8 || F == A_U4; }
+
+// Per-(worker, bucket) statistics.  When a bucket spans whole waves they are
+// wave-uniform: lane l loads worker c0+l's scale and zero (one vector load
+// per 64 workers) and worker w's pair is taken with v_readlane.  (Reading
+// them through the scalar cache instead stalls every pipeline step: scalar
+// loads complete out of order, so the compiler can only wait for all of
+// them, including the next group's.)  Buckets narrower than a wave load each
+// worker's pair per lane, as ordinary in-order vector loads.
+template <class G, int F>
+struct Stats {
+    static constexpr bool WAVE_UNIFORM = G::LPB == WAVE;
+    float ls = 0.0f, lz = 0.0f;  // this lane's worker (c0 + lane), wave-uniform case
+    int32_t c0 = 0;
+
+    __device__ __forceinline__ void load_chunk_of_workers(const float* __restrict__ scale,
+                                                          const float* __restrict__ zero, int64_t nb,
+                                                          int64_t bk, int32_t first, int32_t end) {
+        if constexpr (WAVE_UNIFORM) {
+            c0 = first;
+            const int32_t w = first + lane_id();
+            ls = 0.0f;
+            lz = 0.0f;
+            if (w < end) {
+                ls = scale[(int64_t)w * nb + bk];
+                if constexpr (has_zero(F)) lz = zero[(int64_t)w * nb + bk];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void get(const float* __restrict__ scale, const float* __restrict__ zero,
+                                        int64_t nb, int64_t bk, int32_t w, float& s, float& z) const {
+        if constexpr (WAVE_UNIFORM) {
+            s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), w - c0));
+            z = has_zero(F) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lz), w - c0)) : 0.0f;
+        } else {
+            s = scale[(int64_t)w * nb + bk];
+            z = has_zero(F) ? zero[(int64_t)w * nb + bk] : 0.0f;
+        }
+    }
+};
+
+// Loads of worker w's code chunks for one bucket.
 template <class G, int F, bool FULL>
-__device__ __forceinline__ void load_worker(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-                                            const float* __restrict__ zero, int64_t pbytes, int64_t nb,
-                                            int64_t bk, int64_t base, int64_t n, int32_t w,
-                                            ChunkBits<F> (&c)[G::K], float& s, float& z) {
+__device__ __forceinline__ void load_codes(const uint8_t* __restrict__ codes, int64_t pbytes, int64_t base,
+                                           int64_t n, int32_t w, ChunkBits<F> (&c)[G::K]) {
     const uint8_t* pw = codes + (int64_t)w * pbytes;
-    s = scale[(int64_t)w * nb + bk];
-    z = 0.0f;
-    if constexpr (F == A_U8 || F == A_U4) z = zero[(int64_t)w * nb + bk];
 #pragma unroll
     for (int k = 0; k < G::K; ++k) {
         const int64_t i = base + (int64_t)k * G::LPB * 16;
@@ -95,7 +133,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                                            uint8_t* __restrict__ rq_codes, int64_t rq_pbytes,
                                            float* __restrict__ rq_scale, float* __restrict__ rq_zero,
                                            int64_t bk, float* lds) {
-    constexpr int K = G::K, LPB = G::LPB, UW = 4;
+    constexpr int K = G::K, LPB = G::LPB, UW = 2;
     const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
 
     float a[K][16];
@@ -108,7 +146,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
             if (FULL || i + 16 <= n) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 t = ld_f4(acc + i + 4 * q);
+                    const f32x4 t = ld_stream_f4(acc + i + 4 * q);
                     a[k][4 * q] = t.x; a[k][4 * q + 1] = t.y;
                     a[k][4 * q + 2] = t.z; a[k][4 * q + 3] = t.w;
                 }
@@ -120,39 +158,37 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
         }
     }
 
-    // Software pipeline over groups of UW workers: the loads of group g+1
-    // are in flight while group g's terms are added (in worker order).  The
-    // prefetch clamps the worker index to m-1, so it needs no branch; the
-    // repeated loads of the last group are never added.
-    ChunkBits<F> cur[UW][K];
-    float cs[UW], cz[UW];
+    // Workers are taken 64 at a time (the statistics of one chunk of workers
+    // fit one register across the wave).  Within a chunk, UW register slots
+    // form a rolling prefetch: as soon as worker w's terms have been added
+    // (in worker order), its slot is refilled with worker w+UW, so every
+    // wave always has UW workers' code loads in flight while it computes.
+    // The refill clamps the worker index to the chunk's last worker, so it
+    // needs no branch; the repeated loads past the end are never added.
+    constexpr int32_t CHUNK = Stats<G, F>::WAVE_UNIFORM ? WAVE : 0x7FFFFFFF;
+    Stats<G, F> st;
+    for (int32_t c0 = 0; c0 < m; c0 += CHUNK) {
+        const int32_t cend = m - c0 > CHUNK ? c0 + CHUNK : m;
+        st.load_chunk_of_workers(scale, zero, nb, bk, c0, cend);
+        ChunkBits<F> slot[UW][K];
 #pragma unroll
-    for (int u = 0; u < UW; ++u)
-        load_worker<G, F, FULL>(codes, scale, zero, pbytes, nb, bk, base, n, u < m ? u : m - 1, cur[u],
-                                cs[u], cz[u]);
-    for (int32_t w0 = 0; w0 < m; w0 += UW) {
-        ChunkBits<F> nxt[UW][K];
-        float ns[UW], nz[UW];
+        for (int u = 0; u < UW; ++u)
+            load_codes<G, F, FULL>(codes, pbytes, base, n, c0 + u < cend ? c0 + u : cend - 1, slot[u]);
+        for (int32_t w0 = c0; w0 < cend; w0 += UW) {
 #pragma unroll
-        for (int u = 0; u < UW; ++u) {
-            const int32_t w = w0 + UW + u < m ? w0 + UW + u : m - 1;
-            load_worker<G, F, FULL>(codes, scale, zero, pbytes, nb, bk, base, n, w, nxt[u], ns[u], nz[u]);
-        }
+            for (int u = 0; u < UW; ++u) {
+                if (w0 + u < cend) {
+                    float s, z;
+                    st.get(scale, zero, nb, bk, w0 + u, s, z);
+                    if constexpr (F == A_QSGD) z = s / 7.0f;
 #pragma unroll
-        for (int u = 0; u < UW; ++u) {
-            if (w0 + u >= m) break;
-            if constexpr (F == A_QSGD) cz[u] = cs[u] / 7.0f;
+                    for (int k = 0; k < K; ++k)
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(cur[u][k], j, cs[u], cz[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < UW; ++u) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) cur[u][k] = nxt[u][k];
-            cs[u] = ns[u];
-            cz[u] = nz[u];
+                        for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(slot[u][k], j, s, z);
+                }
+                const int32_t w = w0 + UW + u < cend ? w0 + UW + u : cend - 1;
+                load_codes<G, F, FULL>(codes, pbytes, base, n, w, slot[u]);
+            }
         }
     }
 

@@ -23,8 +23,8 @@ template <bool FULL, bool EF>
 __device__ __forceinline__ void load4(const float* __restrict__ x, const float* __restrict__ ef,
                                       int64_t i, int64_t n, float (&v)[4]) {
     if (FULL || i + 4 <= n) {
-        f32x4 g = ld_f4(x + i);
-        if constexpr (EF) g = ld_f4(ef + i) + g;
+        f32x4 g = ld_stream_f4(x + i);
+        if constexpr (EF) g = ld_stream_f4(ef + i) + g;
         v[0] = g.x; v[1] = g.y; v[2] = g.z; v[3] = g.w;
     } else {
 #pragma unroll

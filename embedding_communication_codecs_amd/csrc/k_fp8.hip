@@ -47,7 +47,7 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
         const int64_t row = r0 + g * RPG + rsub;
-        v[g] = (FULL || row < rows) ? ld_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        v[g] = (FULL || row < rows) ? ld_stream_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int g = 0; g < RG; ++g) {

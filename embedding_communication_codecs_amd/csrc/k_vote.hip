@@ -30,7 +30,7 @@ k_majority_vote(const uint32_t* __restrict__ words, int32_t m, int64_t nvec, int
         for (; w + 4 <= m; w += 4) {
             u32x4 x[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) x[u] = ld_u4(p + (int64_t)(w + u) * stride_vec * 4);
+            for (int u = 0; u < 4; ++u) x[u] = ld_stream_u4(p + (int64_t)(w + u) * stride_vec * 4);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 u32x4 carry = x[u];
@@ -43,7 +43,7 @@ k_majority_vote(const uint32_t* __restrict__ words, int32_t m, int64_t nvec, int
             }
         }
         for (; w < m; ++w) {
-            u32x4 carry = ld_u4(p + (int64_t)w * stride_vec * 4);
+            u32x4 carry = ld_stream_u4(p + (int64_t)w * stride_vec * 4);
 #pragma unroll
             for (int l = 0; l < NLEV; ++l) {
                 const u32x4 t = c[l] & carry;

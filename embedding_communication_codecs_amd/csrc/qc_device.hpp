@@ -31,6 +31,22 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ f32x4 ld_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ u32x4 ld_u4(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Streaming loads, for inputs each kernel reads exactly once: the
+// non-temporal hint keeps them from displacing reused lines.  Measured on
+// MI355X: +10% on the QSGD encoder's read/write mix.
+__device__ __forceinline__ f32x4 ld_stream_f4(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld_stream_u4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld_stream_u2(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ uint32_t ld_stream_u16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
 __device__ __forceinline__ void st_f4(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
