@@ -441,3 +441,74 @@ def test_deterministic_and_stream_async(qc, ora):
         qc.qc_encode_qsgd(xd, None, n, B, 16, 1234, 0, words.t, norm.t, stream=s)
     s.synchronize()
     assert bits_equal(words.host(), a.host())
+
+
+# ====================================================== more workers, shapes
+
+
+@pytest.mark.parametrize("fmt,group", [("u8", 2048), ("u8", 128), ("u4", 1024), ("qsgd", 512), ("sign", 64)])
+@pytest.mark.parametrize("m", [63, 64, 65, 130])
+def test_dequant_accumulate_many_workers(qc, ora, fmt, group, m):
+    """More than 64 workers: statistics are taken 64 workers at a time."""
+    n = 2 * group + 5 if fmt != "sign" else 3 * group + 1
+    code, bits = FMT[fmt]
+    payloads, scale, zero = make_payloads(ora, fmt, m, n, group, seed=700 + m)
+    obits = 4 if fmt in ("u4", "qsgd") else (1 if fmt == "sign" else 8)
+    want = ora.dequant_accumulate(ORA_FMT[fmt], payloads, scale, zero, m, n, group, obits)
+    acc = out_f32(n)
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), None if zero is None else dev(zero), m, n,
+                             group, bits, acc.t, False)
+    sync()
+    assert bits_equal(acc.f32(), want), first_diff(acc.f32(), want)
+
+
+@pytest.mark.parametrize("m", [3000, 65535])
+def test_majority_vote_many_workers(qc, ora, m):
+    n = 96 if m > 10000 else 1000
+    pb = qc.payload_bytes(qc.QC_SIGN, n, 64, 1)
+    arena = synth.host_words(m * pb // 4, 99 + m).view(np.uint8)
+    out = Out(pb)
+    import torch
+
+    qc.qc_majority_vote(dev(arena).view(torch.int32), m, n, out.t.view(torch.int32))
+    sync()
+    want = ora.majority_vote(arena, m, n)
+    assert bits_equal(out.host(), want), first_diff(out.host(), want)
+
+
+def test_random_shapes_all_entry_points(qc, ora):
+    """Seeded sweep: random n, bucket, bits, dims and EF state through every
+    encoder and its decode."""
+    rng = np.random.default_rng(2024)
+    for trial in range(40):
+        n = int(rng.integers(1, 20000))
+        bucket = int(2 ** rng.integers(6, 14))
+        bits = int(rng.choice([8, 4]))
+        sigma = float(10.0 ** rng.integers(-6, 2))
+        x = synth.host_outlier_grad(n, sigma, 0.02, 50.0, seed=trial)
+        ef_h = synth.host_normal(n, sigma * 0.1, seed=1000 + trial)
+        ef_d = dev_ef(ef_h)
+        codes, scale, zero = run_uniform(qc, x, ef_d, bucket, bits)
+        p, s, z = ora.encode_uniform(x, ef_h, bucket, bits)
+        assert bits_equal(codes.host(), p), (trial, n, bucket, bits)
+        assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z) and bits_equal(ef_d.f32(), ef_h)
+        ef_h = synth.host_normal(n, sigma * 0.1, seed=2000 + trial)
+        ef_d = dev_ef(ef_h)
+        off = 4 * int(rng.integers(0, 2**40))
+        words, norm = run_qsgd(qc, x, ef_d, bucket, trial * 7919, off)
+        p, nr = ora.encode_qsgd(x, ef_h, bucket, trial * 7919, off)
+        assert bits_equal(words.host(), p) and bits_equal(norm.f32(), nr), (trial, n, bucket)
+        assert bits_equal(ef_d.f32(), ef_h)
+        xs = synth.host_bf16_bits(x) if trial % 2 else x
+        ef_h = synth.host_normal(n, sigma * 0.1, seed=3000 + trial)
+        ef_d = dev_ef(ef_h)
+        words, ssc = run_sign(qc, xs, ef_d, bucket)
+        p, s = ora.encode_sign(xs, ef_h, bucket)
+        assert bits_equal(words.host(), p) and bits_equal(ssc.f32(), s), (trial, n, bucket)
+        assert bits_equal(ef_d.f32(), ef_h)
+        dim = int(rng.choice([4, 8, 64, 128, 256, 20, 132, 516]))
+        rows = max(1, n // dim)
+        xr = x[: rows * dim] if rows * dim <= n else np.resize(x, rows * dim)
+        c8, s8 = run_fp8(qc, xr, rows, dim)
+        p8, ps8 = ora.encode_fp8_rowwise(xr, rows, dim)
+        assert bits_equal(c8.host(), p8) and bits_equal(s8.f32(), ps8), (trial, rows, dim)
