@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qc_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-UNIFORM, FP8_ROWWISE, QSGD, SIGN = 0, 1, 2, 3
+UNIFORM, FP8_ROWWISE, QSGD, SIGN, TERNARY = 0, 1, 2, 3, 4
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -61,6 +61,9 @@ def lib():
         L.qco_tree_sum.restype = ctypes.c_float
         L.qco_encode_uniform.argtypes = [P, P, I64, I32, I32, P, P, P]
         L.qco_decode_uniform.argtypes = [P, P, P, I64, I32, I32, P]
+        L.qco_encode_uniform_stochastic.argtypes = [P, P, I64, I32, I32, U64, U64, P, P, P]
+        L.qco_encode_ternary.argtypes = [P, P, I64, I32, U64, U64, P, P]
+        L.qco_decode_ternary.argtypes = [P, P, I64, I32, P]
         L.qco_encode_fp8_rowwise.argtypes = [P, I64, I32, P, P]
         L.qco_decode_fp8_rowwise.argtypes = [P, P, I64, I32, P]
         L.qco_encode_qsgd.argtypes = [P, P, I64, I32, U64, U64, P, P]
@@ -139,6 +142,37 @@ def encode_uniform(x, ef, bucket: int, bits: int):
     zero = np.empty(nb, dtype=np.float32)
     lib().qco_encode_uniform(_p(x), _p(ef), n, bucket, bits, _p(payload), _p(scale), _p(zero))
     return payload, scale, zero
+
+
+def encode_uniform_stochastic(x, ef, bucket: int, bits: int, seed: int, elem_offset: int = 0):
+    x = _f32(x)
+    ef = _ef(ef)
+    n = x.size
+    nb = nbuckets(n, bucket)
+    payload = np.empty(payload_bytes(UNIFORM, n, bits), dtype=np.uint8)
+    scale = np.empty(nb, dtype=np.float32)
+    zero = np.empty(nb, dtype=np.float32)
+    lib().qco_encode_uniform_stochastic(_p(x), _p(ef), n, bucket, bits, seed & (2**64 - 1), elem_offset,
+                                        _p(payload), _p(scale), _p(zero))
+    return payload, scale, zero
+
+
+def encode_ternary(x, ef, bucket: int, seed: int, elem_offset: int = 0):
+    x = _f32(x)
+    ef = _ef(ef)
+    n = x.size
+    payload = np.empty(payload_bytes(TERNARY, n, 2), dtype=np.uint8)
+    scale = np.empty(nbuckets(n, bucket), dtype=np.float32)
+    lib().qco_encode_ternary(_p(x), _p(ef), n, bucket, seed & (2**64 - 1), elem_offset, _p(payload),
+                             _p(scale))
+    return payload, scale
+
+
+def decode_ternary(payload, scale, n: int, bucket: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_ternary(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(scale)), n, bucket,
+                             _p(out))
+    return out
 
 
 def decode_uniform(payload, scale, zero, n: int, bucket: int, bits: int):

@@ -52,6 +52,17 @@ static void or_nibble(uint8_t* p, int64_t i, uint32_t code)
     put_word(p, i / 8, get_word(p, i / 8) | (code << (4 * (i % 8))));
 }
 
+/* 2-bit code of element i (least significant pair first in each word). */
+static uint32_t get_crumb(const uint8_t* p, int64_t i)
+{
+    return (get_word(p, i / 16) >> (2 * (i % 16))) & 0x3u;
+}
+
+static void or_crumb(uint8_t* p, int64_t i, uint32_t code)
+{
+    put_word(p, i / 16, get_word(p, i / 16) | (code << (2 * (i % 16))));
+}
+
 static uint32_t get_bit(const uint8_t* p, int64_t i)
 {
     return (get_word(p, i / 32) >> (i % 32)) & 1u;
@@ -67,11 +78,26 @@ int64_t qco_payload_bytes(int32_t fmt, int64_t n, int32_t bits)
     int64_t code_bytes;
     if (fmt == QCO_SIGN)
         code_bytes = 4 * ceil_div(n, 32);
+    else if (fmt == QCO_TERNARY || (fmt == QCO_UNIFORM && bits == 2))
+        code_bytes = 4 * ceil_div(n, 16);
     else if (fmt == QCO_QSGD || (fmt == QCO_UNIFORM && bits == 4))
         code_bytes = 4 * ceil_div(n, 8);
     else
         code_bytes = n; /* one byte per element: INT8 and FP8 */
     return ceil_div(code_bytes, 16) * 16;
+}
+
+/* A uniform draw in [0, 1) for global element index g: the top 24 bits of
+ * word g%4 of Philox4x32-10 with key = seed (low word first) and counter =
+ * (g/4 low word, g/4 high word, 0, 0), scaled by 2^-24 (exact). */
+static float uniform_draw(uint64_t seed, uint64_t g)
+{
+    const uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
+    const uint64_t blk = g >> 2;
+    const uint32_t ctr[4] = { (uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u };
+    uint32_t r[4];
+    qco_philox4x32_10(ctr, key, r);
+    return (float)(r[g & 3u] >> 8) * 0x1p-24f;
 }
 
 /* ------------------------------------------------------------------ */
@@ -198,8 +224,32 @@ static float uniform_dq(uint32_t q, float scale, float zero)
     return p + zero;
 }
 
-void qco_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket,
-                        int32_t bits, uint8_t* payload, float* scale, float* zero)
+/* Uniform codes of 8, 4 or 2 bits: byte i, nibble i, or 2-bit field i. */
+static void put_uniform_code(uint8_t* payload, int64_t i, int32_t bits, uint32_t q)
+{
+    if (bits == 8)
+        payload[i] = (uint8_t)q;
+    else if (bits == 4)
+        or_nibble(payload, i, q);
+    else
+        or_crumb(payload, i, q);
+}
+
+static uint32_t get_uniform_code(const uint8_t* payload, int64_t i, int32_t bits)
+{
+    if (bits == 8)
+        return payload[i];
+    return bits == 4 ? get_nibble(payload, i) : get_crumb(payload, i);
+}
+
+/* The affine grid of one bucket, then one code per element: nearest level
+ * (round half to even) or, when `stochastic`, the lower level plus one with
+ * probability equal to the fractional part [QCD, "Quantization Schemes":
+ * stochastic quantization; GQC, "Quantization Schemes"], the draw for
+ * element i being uniform_draw(seed, elem_offset + i). */
+static void encode_uniform_any(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                               int stochastic, uint64_t seed, uint64_t elem_offset,
+                               uint8_t* payload, float* scale, float* zero)
 {
     const uint32_t L = (1u << bits) - 1u;
     const int64_t nb = ceil_div(n, bucket);
@@ -223,19 +273,23 @@ void qco_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket,
 
         const float sc = (mx - mn) / (float)L;
         for (int64_t j = 0; j < cnt; ++j) {
+            const int64_t i = lo + j;
             uint32_t q = 0;
             if (sc != 0.0f) {
                 float t = (v[j] - mn) / sc;
-                float r = rintf(t);
+                float r;
+                if (stochastic) {
+                    float fl = floorf(t);
+                    float frac = t - fl; /* exact */
+                    r = fl + (uniform_draw(seed, elem_offset + (uint64_t)i) < frac ? 1.0f : 0.0f);
+                } else {
+                    r = rintf(t);
+                }
                 if (r < 0.0f) r = 0.0f;
                 if (r > (float)L) r = (float)L;
                 q = (uint32_t)r;
             }
-            const int64_t i = lo + j;
-            if (bits == 8)
-                payload[i] = (uint8_t)q;
-            else
-                or_nibble(payload, i, q);
+            put_uniform_code(payload, i, bits, q);
             if (ef)
                 ef[i] = v[j] - uniform_dq(q, sc, mn);
         }
@@ -245,13 +299,24 @@ void qco_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket,
     free(v);
 }
 
+void qco_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket,
+                        int32_t bits, uint8_t* payload, float* scale, float* zero)
+{
+    encode_uniform_any(x, ef, n, bucket, bits, 0, 0, 0, payload, scale, zero);
+}
+
+void qco_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t bucket,
+                                   int32_t bits, uint64_t seed, uint64_t elem_offset,
+                                   uint8_t* payload, float* scale, float* zero)
+{
+    encode_uniform_any(x, ef, n, bucket, bits, 1, seed, elem_offset, payload, scale, zero);
+}
+
 void qco_decode_uniform(const uint8_t* payload, const float* scale, const float* zero,
                         int64_t n, int32_t bucket, int32_t bits, float* out)
 {
-    for (int64_t i = 0; i < n; ++i) {
-        uint32_t q = (bits == 8) ? payload[i] : get_nibble(payload, i);
-        out[i] = uniform_dq(q, scale[i / bucket], zero[i / bucket]);
-    }
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = uniform_dq(get_uniform_code(payload, i, bits), scale[i / bucket], zero[i / bucket]);
 }
 
 /* ------------------------------------------------------------------ */
@@ -305,11 +370,9 @@ void qco_decode_fp8_rowwise(const uint8_t* payload, const float* scale,
  * fp32).  Reading: a code is a sign bit (bit 3) and a level l in 0..7
  * (bits 0-2); level l stands for l * d with d = ||v||_2 / 7 over the
  * bucket.  |v| / d is rounded down or up at random with P(up) equal to its
- * fractional part, which makes DQ unbiased.  The uniform draw for element
- * g (global index) is word g%4 of Philox4x32-10 with key = seed (low word
- * first) and counter = (g/4 low word, g/4 high word, 0, 0); its top 24
- * bits form u = (r >> 8) * 2^-24 and the element rounds up iff u < frac.
- * A level-0 code is always 0 (no negative zero); DQ of code 0 is +0. */
+ * fractional part, which makes DQ unbiased: the element with global index
+ * g rounds up iff uniform_draw(seed, g) < frac.  A level-0 code is always 0
+ * (no negative zero); DQ of code 0 is +0. */
 
 static float qsgd_dq(uint32_t code, float d)
 {
@@ -325,7 +388,6 @@ void qco_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket,
                      uint8_t* payload, float* norm)
 {
     const int64_t nb = ceil_div(n, bucket);
-    const uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
     memset(payload, 0, (size_t)qco_payload_bytes(QCO_QSGD, n, 4));
     float* v = (float*)malloc((size_t)bucket * sizeof(float));
     float* sq = (float*)malloc((size_t)bucket * sizeof(float));
@@ -348,12 +410,7 @@ void qco_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket,
                 float t = fabsf(v[j]) / d;
                 float fl = floorf(t);
                 float frac = t - fl; /* exact */
-                uint64_t g = elem_offset + (uint64_t)i;
-                uint64_t blk = g >> 2;
-                uint32_t ctr[4] = { (uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u };
-                uint32_t r[4];
-                qco_philox4x32_10(ctr, key, r);
-                float u = (float)(r[g & 3u] >> 8) * 0x1p-24f;
+                float u = uniform_draw(seed, elem_offset + (uint64_t)i);
                 uint32_t level = (uint32_t)fl + (u < frac ? 1u : 0u);
                 if (level > 7u) level = 7u;
                 if (level != 0u)
@@ -376,6 +433,66 @@ void qco_decode_qsgd(const uint8_t* payload, const float* norm, int64_t n,
         float d = norm[i / bucket] / 7.0f;
         out[i] = qsgd_dq(get_nibble(payload, i), d);
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* TernGrad  [QCD, "Quantized SGD Algorithms": TernGrad]                */
+/* ------------------------------------------------------------------ */
+/* Three levels {-1, 0, +1} times a scale.  Readings: the scale is
+ * s = max |v| over the bucket (the pages give one scale per layer; a bucket
+ * plays that role here, as for the other codecs); element v becomes sign(v)
+ * with probability |v|/s and 0 otherwise, so E[DQ] = v: it is nonzero iff
+ * uniform_draw(seed, g) < fl(|v| / s).  A 2-bit code holds "nonzero" in
+ * bit 0 and "negative" in bit 1 (0 = zero, 1 = +s, 3 = -s; 2 never
+ * occurs).  s == 0 gives all codes 0.  DQ = code ? (code & 2 ? -s : s) : +0. */
+
+static float ternary_dq(uint32_t code, float s)
+{
+    if ((code & 1u) == 0u)
+        return 0.0f;
+    return (code & 2u) ? -s : s;
+}
+
+void qco_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket,
+                        uint64_t seed, uint64_t elem_offset,
+                        uint8_t* payload, float* scale)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    memset(payload, 0, (size_t)qco_payload_bytes(QCO_TERNARY, n, 2));
+    float* v = (float*)malloc((size_t)bucket * sizeof(float));
+
+    for (int64_t k = 0; k < nb; ++k) {
+        const int64_t lo = k * bucket;
+        const int64_t cnt = (lo + bucket <= n) ? bucket : n - lo;
+
+        float s = 0.0f;
+        for (int64_t j = 0; j < cnt; ++j) {
+            v[j] = ef ? ef[lo + j] + x[lo + j] : x[lo + j];
+            if (fabsf(v[j]) > s) s = fabsf(v[j]);
+        }
+
+        for (int64_t j = 0; j < cnt; ++j) {
+            const int64_t i = lo + j;
+            uint32_t code = 0;
+            if (s != 0.0f) {
+                float p = fabsf(v[j]) / s;
+                if (uniform_draw(seed, elem_offset + (uint64_t)i) < p)
+                    code = (v[j] < 0.0f) ? 3u : 1u;
+            }
+            or_crumb(payload, i, code);
+            if (ef)
+                ef[i] = v[j] - ternary_dq(code, s);
+        }
+        scale[k] = s;
+    }
+    free(v);
+}
+
+void qco_decode_ternary(const uint8_t* payload, const float* scale, int64_t n,
+                        int32_t bucket, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ternary_dq(get_crumb(payload, i), scale[i / bucket]);
 }
 
 /* ------------------------------------------------------------------ */
@@ -439,14 +556,14 @@ float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,
 {
     const int64_t k = i / group;
     switch (fmt) {
-    case QCO_UNIFORM: {
-        uint32_t q = (bits == 8) ? payload[i] : get_nibble(payload, i);
-        return uniform_dq(q, scale[k], zero[k]);
-    }
+    case QCO_UNIFORM:
+        return uniform_dq(get_uniform_code(payload, i, bits), scale[k], zero[k]);
     case QCO_FP8_ROWWISE:
         return qco_e4m3_to_f32(payload[i]) * scale[k];
     case QCO_QSGD:
         return qsgd_dq(get_nibble(payload, i), scale[k] / 7.0f);
+    case QCO_TERNARY:
+        return ternary_dq(get_crumb(payload, i), scale[k]);
     default: /* QCO_SIGN */
         return get_bit(payload, i) ? -scale[k] : scale[k];
     }

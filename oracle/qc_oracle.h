@@ -25,8 +25,9 @@
  *     the code bytes rounded up to 16.  Every payload byte is written;
  *     bytes after the last code are zero.
  *   - Low-bit codes are packed least-significant-bit first: element i of a
- *     4-bit payload is bits 4*(i%8)..4*(i%8)+3 of 32-bit word i/8, and of a
- *     1-bit payload it is bit i%32 of word i/32 (words little-endian).
+ *     4-bit payload is bits 4*(i%8)..4*(i%8)+3 of 32-bit word i/8, of a
+ *     2-bit payload bits 2*(i%16)..2*(i%16)+1 of word i/16, and of a 1-bit
+ *     payload bit i%32 of word i/32 (words little-endian).
  */
 #ifndef QC_ORACLE_H
 #define QC_ORACLE_H
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-enum { QCO_UNIFORM = 0, QCO_FP8_ROWWISE = 1, QCO_QSGD = 2, QCO_SIGN = 3 };
+enum { QCO_UNIFORM = 0, QCO_FP8_ROWWISE = 1, QCO_QSGD = 2, QCO_SIGN = 3, QCO_TERNARY = 4 };
 
 /* Bytes of one payload of n elements (see conventions above). */
 int64_t qco_payload_bytes(int32_t fmt, int64_t n, int32_t bits);
@@ -54,9 +55,14 @@ void    qco_e4m3_from_f32_n(const float* y, int64_t n, uint8_t* out);
 /* Contiguous pairwise sum of len terms, len padded with +0 to `pow2len`. */
 float qco_tree_sum(const float* terms, int64_t len, int64_t pow2len);
 
-/* Uniform affine quantizer with optional error feedback (ef may be NULL). */
+/* Uniform affine quantizer (bits 8, 4 or 2) with optional error feedback
+ * (ef may be NULL): nearest level, or stochastic rounding keyed by
+ * (seed, elem_offset + index) as for QSGD. */
 void qco_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket,
                         int32_t bits, uint8_t* payload, float* scale, float* zero);
+void qco_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t bucket,
+                                   int32_t bits, uint64_t seed, uint64_t elem_offset,
+                                   uint8_t* payload, float* scale, float* zero);
 void qco_decode_uniform(const uint8_t* payload, const float* scale, const float* zero,
                         int64_t n, int32_t bucket, int32_t bits, float* out);
 
@@ -81,6 +87,14 @@ void qco_encode_sign(const void* x, int32_t x_bf16, float* ef, int64_t n,
                      int32_t bucket, uint8_t* payload, float* scale);
 void qco_decode_sign(const uint8_t* payload, const float* scale, int64_t n,
                      int32_t bucket, float* out);
+
+/* TernGrad: codes {0, +1, -1} (2 bits each) times the bucket's max |v|,
+ * nonzero with probability |v| / max|v| (ef may be NULL). */
+void qco_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket,
+                        uint64_t seed, uint64_t elem_offset,
+                        uint8_t* payload, float* scale);
+void qco_decode_ternary(const uint8_t* payload, const float* scale, int64_t n,
+                        int32_t bucket, float* out);
 
 /* Element i of a payload decoded to fp32, for any format. */
 float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,

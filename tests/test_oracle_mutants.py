@@ -20,14 +20,37 @@ def _load(name, path):
     return mod
 
 
-PINS = _load("oracle_pins_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins.py"))
+PIN_MODULES = [
+    _load("oracle_pins_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins.py")),
+    _load("oracle_pins_stochastic_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_stochastic.py")),
+]
+
+
+def pin(name):
+    for mod in PIN_MODULES:
+        if hasattr(mod, name):
+            return getattr(mod, name)
+    raise KeyError(name)
 
 # (name, text in qc_oracle.c, replacement, pins expected to catch it)
 MUTANTS = [
     ("uniform_keeps_negative_zero", "    mn = mn + 0.0f; /* -0 -> +0 */\n", "",
      ["test_uniform_constant_and_signed_zero"]),
-    ("uniform_rounds_down", "float r = rintf(t);", "float r = floorf(t);",
+    ("uniform_rounds_down", "r = rintf(t);", "r = floorf(t);",
      ["test_uniform_brute_force_nearest"]),
+    ("uniform_crumbs_msb_first", "put_word(p, i / 16, get_word(p, i / 16) | (code << (2 * (i % 16))));",
+     "put_word(p, i / 16, get_word(p, i / 16) | (code << (2 * (15 - i % 16))));",
+     ["test_uniform_packing_known_answer"]),
+    ("stochastic_rounds_wrong_way", "< frac ? 1.0f : 0.0f", "> frac ? 1.0f : 0.0f",
+     ["test_stochastic_uniform_follows_library_draws", "test_stochastic_uniform_unbiased"]),
+    ("stochastic_ignores_offset", "r = fl + (uniform_draw(seed, elem_offset + (uint64_t)i)",
+     "r = fl + (uniform_draw(seed, (uint64_t)i)", ["test_stochastic_uniform_follows_library_draws"]),
+    ("ternary_half_probability", "float p = fabsf(v[j]) / s;", "float p = fabsf(v[j]) / (2.0f * s);",
+     ["test_ternary_follows_library_draws", "test_ternary_unbiased_and_probability"]),
+    ("ternary_sign_flip", "code = (v[j] < 0.0f) ? 3u : 1u;", "code = (v[j] < 0.0f) ? 1u : 3u;",
+     ["test_ternary_closed_forms"]),
+    ("ternary_mean_scale", "if (fabsf(v[j]) > s) s = fabsf(v[j]);", "s = s + fabsf(v[j]) / (float)cnt;",
+     ["test_ternary_follows_library_draws", "test_ternary_closed_forms"]),
     ("uniform_dq_wrong_sign", "    return p + zero;", "    return p - zero;",
      ["test_uniform_error_bound_and_extremes", "test_uniform_error_feedback_invariants"]),
     ("uniform_levels_off_by_one", "const float sc = (mx - mn) / (float)L;",
@@ -51,9 +74,12 @@ MUTANTS = [
      ["test_qsgd_deterministic_on_grid", "test_qsgd_levels_bracket_value"]),
     ("qsgd_rounds_wrong_way", "(u < frac ? 1u : 0u)", "(u > frac ? 1u : 0u)",
      ["test_qsgd_unbiased"]),
-    ("qsgd_wrong_word", "float u = (float)(r[g & 3u] >> 8) * 0x1p-24f;",
-     "float u = (float)(r[(g + 1) & 3u] >> 8) * 0x1p-24f;", ["test_qsgd_draws_follow_library_philox"]),
-    ("qsgd_ignores_offset", "uint64_t g = elem_offset + (uint64_t)i;", "uint64_t g = (uint64_t)i;",
+    ("draw_wrong_word", "return (float)(r[g & 3u] >> 8) * 0x1p-24f;",
+     "return (float)(r[(g + 1) & 3u] >> 8) * 0x1p-24f;", ["test_qsgd_draws_follow_library_philox"]),
+    ("draw_fewer_bits", "return (float)(r[g & 3u] >> 8) * 0x1p-24f;",
+     "return (float)(r[g & 3u] >> 16) * 0x1p-16f;", ["test_stochastic_uniform_draw_resolution"]),
+    ("qsgd_ignores_offset", "float u = uniform_draw(seed, elem_offset + (uint64_t)i);",
+     "float u = uniform_draw(seed, (uint64_t)i);",
      ["test_qsgd_counter_offsets_compose", "test_qsgd_draws_follow_library_philox"]),
     ("qsgd_drops_square", "sq[j] = v[j] * v[j];", "sq[j] = fabsf(v[j]);",
      ["test_qsgd_deterministic_on_grid"]),
@@ -98,7 +124,7 @@ def _run_pin(fn, mod, rocrand_philox):
         kw["rocrand_philox"] = rocrand_philox
     variants = [{}]
     if "bits" in sig.parameters:
-        variants = [{"bits": 8}, {"bits": 4}]
+        variants = [{"bits": 8}, {"bits": 4}, {"bits": 2}]
     if "fmt" in sig.parameters:
         variants = [{"fmt": f} for f in ("fp8", "qsgd", "sign", "int4")]
     for v in variants:
@@ -109,9 +135,9 @@ def _run_pin(fn, mod, rocrand_philox):
 def test_pins_reject_mutant(mutant_dir, rocrand_philox, name, old, new, pins):
     mod = _build_mutant(mutant_dir, name, old, new)
     caught = []
-    for pin in pins:
+    for name_ in pins:
         try:
-            _run_pin(getattr(PINS, pin), mod, rocrand_philox)
+            _run_pin(pin(name_), mod, rocrand_philox)
         except AssertionError:
-            caught.append(pin)
+            caught.append(name_)
     assert caught, f"no pin rejected mutant {name}"

@@ -40,7 +40,7 @@ def test_numeric_example_payload_bytes(ora):
     assert 4 * g["lookups"] == g["rowwise_scale_bytes_fp32"]
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_uniform_ratio_below_nominal(ora, bits):
     g = golden("compression_ratios.json")
     n = 1 << 20
@@ -208,7 +208,7 @@ def _dq_exact(q, scale, zero):
     return Fraction(float(np.float32(q) * np.float32(scale))) + Fraction(float(zero))
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_uniform_brute_force_nearest(ora, bits):
     """On tiny buckets every code is the nearest grid point, computed from
     exact rationals over all 2^b codes (ties can go either way only when the
@@ -228,7 +228,8 @@ def test_uniform_brute_force_nearest(ora, bits):
             q = payload[:n].astype(int)
         else:
             words = payload.view(np.uint32)
-            q = np.array([(int(words[i // 8]) >> (4 * (i % 8))) & 15 for i in range(n)])
+            per = 32 // bits
+            q = np.array([(int(words[i // per]) >> (bits * (i % per))) & L for i in range(n)])
         for i in range(n):
             if s == 0.0:
                 assert q[i] == 0
@@ -241,7 +242,7 @@ def test_uniform_brute_force_nearest(ora, bits):
                 assert abs(t - (math.floor(t) + Fraction(1, 2))) <= 4 * U * (abs(t) + 1)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_uniform_error_bound_and_extremes(ora, bits):
     n, B = 3 * 4096 + 123, 4096
     x = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=5)
@@ -268,6 +269,9 @@ def test_uniform_packing_known_answer(ora):
     assert s[0] == 1.0 and z[0] == 0.0
     w = p.view(np.uint32)
     assert w[0] == 0x76543210 and w[1] == 0xFEDCBA98 and w[2] == 0 and w[3] == 0
+    # values 0..3 repeated: min 0, max 3 -> scale 1 -> 2-bit codes i%4
+    p, s, z = ora.encode_uniform(np.array([0, 1, 2, 3] * 4, np.float32), None, 64, 2)
+    assert s[0] == 1.0 and p.view(np.uint32)[0] == 0xE4E4E4E4 and not p[4:].any()
     x = np.arange(256, dtype=np.float32)
     p, s, z = ora.encode_uniform(x, None, 256, 8)
     assert np.array_equal(p, np.arange(256, dtype=np.uint8))
@@ -291,7 +295,7 @@ def test_uniform_constant_and_signed_zero(ora):
     assert s[0] == 0.0 and math.copysign(1, z[0]) == 1.0  # -0 canonicalized to +0
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_uniform_error_feedback_invariants(ora, bits):
     """[QCD "Error Feedback for Quantization"; GCQC "Error feedback ..."]:
     per step e_new + DQ = e_old + g up to two roundings, and over steps the
@@ -639,7 +643,7 @@ def test_accumulate_vs_exact_sum(ora):
     assert np.array_equal(acc2, (start + np.asarray(terms[0], np.float32)).astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "qsgd", "sign", "int4"])
+@pytest.mark.parametrize("fmt", ["fp8", "qsgd", "sign", "int4", "int2", "ternary"])
 def test_accumulate_other_formats(ora, fmt):
     m, n = 3, 2048
     parts, sc, ze, terms = [], [], [], []
@@ -657,10 +661,15 @@ def test_accumulate_other_formats(ora, fmt):
             p, s = ora.encode_sign(g, None, 256)
             z, F, grp, bits = None, ora.SIGN, 256, 1
             t = ora.decode_sign(p, s, n, 256)
+        elif fmt == "ternary":
+            p, s = ora.encode_ternary(g, None, 256, 9 + w)
+            z, F, grp, bits = None, ora.TERNARY, 256, 2
+            t = ora.decode_ternary(p, s, n, 256)
         else:
-            p, s, z = ora.encode_uniform(g, None, 256, 4)
-            F, grp, bits = ora.UNIFORM, 256, 4
-            t = ora.decode_uniform(p, s, z, n, 256, 4)
+            b = 4 if fmt == "int4" else 2
+            p, s, z = ora.encode_uniform(g, None, 256, b)
+            F, grp, bits = ora.UNIFORM, 256, b
+            t = ora.decode_uniform(p, s, z, n, 256, b)
         parts.append(p)
         sc.append(s)
         ze.append(z)
