@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     QC_OK,
     QC_QSGD,
     QC_SIGN,
+    QC_TERNARY,
     QC_UNIFORM,
     QcError,
     lib,
@@ -32,7 +33,9 @@ from .binding import (  # noqa: F401
     qc_encode_fp8_rowwise,
     qc_encode_qsgd,
     qc_encode_sign,
+    qc_encode_ternary,
     qc_encode_uniform,
+    qc_encode_uniform_stochastic,
     qc_majority_vote,
     qc_payload_bytes,
     qc_status_str,

@@ -18,13 +18,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqc.so")
 
 QC_OK, QC_ERR_ARG, QC_ERR_ALIGN, QC_ERR_UNSUPPORTED, QC_ERR_LAUNCH = 0, 1, 2, 3, 4
-QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN = 0, 1, 2, 3
+QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN, QC_TERNARY = 0, 1, 2, 3, 4
 QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
 
 EXPORTS = (
-    "qc_encode_uniform", "qc_encode_fp8_rowwise", "qc_encode_qsgd", "qc_encode_sign",
-    "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
+    "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_fp8_rowwise", "qc_encode_qsgd",
+    "qc_encode_ternary", "qc_encode_sign", "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
 
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
         sig = {
             "qc_encode_uniform": [P, P, I64, I32, I32, P, P, P, P],
+            "qc_encode_uniform_stochastic": [P, P, I64, I32, I32, U64, U64, P, P, P, P],
+            "qc_encode_ternary": [P, P, I64, I32, U64, U64, P, P, P],
             "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
             "qc_encode_qsgd": [P, P, I64, I32, I32, U64, U64, P, P, P],
             "qc_encode_sign": [P, I32, P, I64, I32, P, P, P],
@@ -115,12 +117,33 @@ def _check(status: int):
 # ------------------------------------------------------------ entry points
 
 
+UNIFORM_BITS = (2, 4, 8)
+
+
 def qc_encode_uniform(x, ef, n, bucket, bits, codes, scale, zero, stream=None):
     nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
-    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in (4, 8) and n >= 0 else None
+    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in UNIFORM_BITS and n >= 0 else None
     _check(lib().qc_encode_uniform(
         _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, bits, _ptr(codes, pb, "codes"),
         _ptr(scale, 4 * nb, "scale"), _ptr(zero, 4 * nb, "zero"), _stream(stream)))
+
+
+def qc_encode_uniform_stochastic(x, ef, n, bucket, bits, seed, elem_offset, codes, scale, zero,
+                                 stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in UNIFORM_BITS and n >= 0 else None
+    _check(lib().qc_encode_uniform_stochastic(
+        _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, bits, seed & (2**64 - 1), elem_offset,
+        _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"), _ptr(zero, 4 * nb, "zero"),
+        _stream(stream)))
+
+
+def qc_encode_ternary(x, ef, n, bucket, seed, elem_offset, words, scale, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_TERNARY, n, bucket, 2) if n >= 0 else None
+    _check(lib().qc_encode_ternary(
+        _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, seed & (2**64 - 1), elem_offset,
+        _ptr(words, pb, "words"), _ptr(scale, 4 * nb, "scale"), _stream(stream)))
 
 
 def qc_encode_fp8_rowwise(x, rows, dim, codes, scale, stream=None):
@@ -161,7 +184,7 @@ def qc_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, acc, accum
     nb = nbuckets(n, group) if n > 0 and group > 0 else 0
     pb = payload_bytes(fmt, n, group, bits) if n >= 0 else -1
     mm = max(m, 0)
-    rq_pb = payload_bytes(QC_UNIFORM, n, group, bits) if bits in (4, 8) and n >= 0 else None
+    rq_pb = payload_bytes(QC_UNIFORM, n, group, bits) if bits in UNIFORM_BITS and n >= 0 else None
     _check(lib().qc_dequant_accumulate(
         fmt, _ptr(codes, mm * pb if pb >= 0 else None, "codes"), _ptr(scale, 4 * mm * nb, "scale"),
         _ptr(zero, 4 * mm * nb, "zero"), m, n, group, bits, _ptr(acc, 4 * n, "acc"),

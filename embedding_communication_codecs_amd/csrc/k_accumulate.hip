@@ -26,7 +26,7 @@
 namespace qc {
 namespace {
 
-enum { A_U8 = 0, A_U4 = 1, A_FP8 = 2, A_QSGD = 3, A_SIGN = 4 };
+enum { A_U8 = 0, A_U4 = 1, A_FP8 = 2, A_QSGD = 3, A_SIGN = 4, A_U2 = 5, A_TER = 6 };
 
 // Raw code bits of a 16-element chunk starting at element i of a payload.
 template <int F>
@@ -42,6 +42,8 @@ __device__ __forceinline__ ChunkBits<F> load_chunk(const uint8_t* __restrict__ p
     } else if constexpr (F == A_U4 || F == A_QSGD) {
         const u32x2 h = ld_stream_u2(p + i / 2);
         r.v = u32x4{h.x, h.y, 0u, 0u};
+    } else if constexpr (F == A_U2 || F == A_TER) {
+        r.v = u32x4{ld_stream_u32(p + i / 4), 0u, 0u, 0u};
     } else {
         const uint32_t h = ld_stream_u16(p + i / 8);
         r.v = u32x4{h, 0u, 0u, 0u};
@@ -61,6 +63,12 @@ __device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s,
     } else if constexpr (F == A_U4) {
         const float p = (float)((words[j >> 3] >> (4 * (j & 7))) & 0xFu) * s;
         return p + z;
+    } else if constexpr (F == A_U2) {
+        const float p = (float)((words[0] >> (2 * j)) & 0x3u) * s;
+        return p + z;
+    } else if constexpr (F == A_TER) {
+        const uint32_t code = (words[0] >> (2 * j)) & 0x3u;
+        return (code & 1u) ? ((code & 2u) ? -s : s) : 0.0f;
     } else if constexpr (F == A_QSGD) {
         const uint32_t code = (words[j >> 3] >> (4 * (j & 7))) & 0xFu;
         const uint32_t level = code & 7u;
@@ -71,7 +79,7 @@ __device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s,
     }
 }
 
-constexpr bool has_zero(int F) { return F == A_U8 || F == A_U4; }
+constexpr bool has_zero(int F) { return F == A_U8 || F == A_U4 || F == A_U2; }
 
 // Per-(worker, bucket) statistics.  When a bucket spans whole waves they are
 // wave-uniform: lane l loads worker c0+l's scale and zero (one vector load
@@ -252,7 +260,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                 o.z = q[8] | (q[9] << 8) | (q[10] << 16) | (q[11] << 24);
                 o.w = q[12] | (q[13] << 8) | (q[14] << 16) | (q[15] << 24);
                 if (FULL || i < rq_pbytes) st_u4(rq_codes + i, o);
-            } else {
+            } else if constexpr (RQBITS == 4) {
                 uint32_t lo = 0, hi = 0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -263,6 +271,11 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                     st_u32(rq_codes + i / 2, lo);
                     st_u32(rq_codes + i / 2 + 4, hi);
                 }
+            } else {
+                uint32_t word = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) word |= q[j] << (2 * j);
+                if (FULL || i / 4 < rq_pbytes) st_u32(rq_codes + i / 4, word);
             }
         }
         if (bucket_leader<G>()) {
@@ -333,23 +346,19 @@ hipError_t launch_fmt(const void* codes, const float* scale, const float* zero, 
         int64_t blocks = grid_for(nb, G::BPB);
         blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
         const dim3 grid((unsigned)blocks), block(G::THREADS);
-        const int64_t rq_pbytes = bits == 8 ? (n + 15) / 16 * 16 : ((n + 7) / 8 * 4 + 15) / 16 * 16;
+        const int64_t rq_code_bytes = bits == 8 ? n : (bits == 4 ? (n + 7) / 8 * 4 : (n + 15) / 16 * 4);
+        const int64_t rq_pbytes = (rq_code_bytes + 15) / 16 * 16;
         if (rq_codes == nullptr) {
             hipLaunchKernelGGL((k_dequant_acc<G, F, 8, false>), grid, block, 0, stream,
                                (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
                                (int32_t)accumulate, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr,
                                (float*)nullptr);
-        } else if constexpr (F == A_U8 || F == A_U4) {
-            if (bits == 8)
-                hipLaunchKernelGGL((k_dequant_acc<G, F, 8, true>), grid, block, 0, stream,
-                                   (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
-                                   (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale,
-                                   rq_zero);
-            else
-                hipLaunchKernelGGL((k_dequant_acc<G, F, 4, true>), grid, block, 0, stream,
-                                   (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
-                                   (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale,
-                                   rq_zero);
+        } else if constexpr (F == A_U8 || F == A_U4 || F == A_U2) {
+            // requantization to the input's own bit width
+            constexpr int RQB = F == A_U8 ? 8 : (F == A_U4 ? 4 : 2);
+            hipLaunchKernelGGL((k_dequant_acc<G, F, RQB, true>), grid, block, 0, stream,
+                               (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                               (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale, rq_zero);
         } else {
             return hipErrorInvalidValue;
         }
@@ -369,7 +378,10 @@ hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float
             if (bits == 8)
                 return launch_fmt<A_U8>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
                                         accumulate, rq_codes, rq_scale, rq_zero, stream);
-            return launch_fmt<A_U4>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+            if (bits == 4)
+                return launch_fmt<A_U4>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                        accumulate, rq_codes, rq_scale, rq_zero, stream);
+            return launch_fmt<A_U2>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
                                     accumulate, rq_codes, rq_scale, rq_zero, stream);
         case 1:
             return launch_fmt<A_FP8>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
@@ -377,6 +389,9 @@ hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float
         case 2:
             return launch_fmt<A_QSGD>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
                                       accumulate, rq_codes, rq_scale, rq_zero, stream);
+        case 4:
+            return launch_fmt<A_TER>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
+                                     accumulate, rq_codes, rq_scale, rq_zero, stream);
         default:
             return launch_fmt<A_SIGN>(codes, scale, zero, m, n, group, bits, payload_bytes, acc,
                                       accumulate, rq_codes, rq_scale, rq_zero, stream);

@@ -16,13 +16,15 @@
 namespace qc {
 namespace {
 
-enum { F_U8 = 0, F_U4 = 1, F_FP8 = 2, F_QSGD = 3, F_SIGN = 4 };
+enum { F_U8 = 0, F_U4 = 1, F_FP8 = 2, F_QSGD = 3, F_SIGN = 4, F_U2 = 5, F_TER = 6 };
 
+// The code bits of chunk c (elements 4c..4c+3) in the low bits.
 template <int F>
 __device__ __forceinline__ uint32_t chunk_word(const uint8_t* __restrict__ codes, int64_t c) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(codes);
     if constexpr (F == F_U8 || F == F_FP8) return w[c];
     else if constexpr (F == F_U4 || F == F_QSGD) return w[c >> 1] >> ((c & 1) * 16);
+    else if constexpr (F == F_U2 || F == F_TER) return w[c >> 2] >> ((c & 3) * 8);
     else return w[c >> 3] >> ((c & 7) * 4);
 }
 
@@ -35,6 +37,12 @@ __device__ __forceinline__ float chunk_value(uint32_t w, int j, float s, float z
     } else if constexpr (F == F_U4) {
         const float p = (float)((w >> (4 * j)) & 0xFu) * s;
         return p + z;
+    } else if constexpr (F == F_U2) {
+        const float p = (float)((w >> (2 * j)) & 0x3u) * s;
+        return p + z;
+    } else if constexpr (F == F_TER) {
+        const uint32_t code = (w >> (2 * j)) & 0x3u;
+        return (code & 1u) ? ((code & 2u) ? -s : s) : 0.0f;
     } else if constexpr (F == F_FP8) {
         return e4m3_decode((w >> (8 * j)) & 0xFFu) * s;
     } else if constexpr (F == F_QSGD) {
@@ -63,7 +71,7 @@ __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, c
             const int64_t bk = POW2 ? ((c << 2) >> gshift) : ((c << 2) / group);
             w[u] = chunk_word<F>(codes, c);
             s[u] = scale[bk];
-            if constexpr (F == F_U8 || F == F_U4) z[u] = zero[bk];
+            if constexpr (F == F_U8 || F == F_U4 || F == F_U2) z[u] = zero[bk];
         }
     }
 #pragma unroll
@@ -118,8 +126,11 @@ hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, con
                          int64_t n, int32_t group, int32_t bits, float* out, hipStream_t stream) {
     switch (fmt) {
         case 0:  // uniform
-            return bits == 8 ? launch<F_U8, true>(codes, scale, zero, n, group, out, stream)
-                             : launch<F_U4, true>(codes, scale, zero, n, group, out, stream);
+            if (bits == 8) return launch<F_U8, true>(codes, scale, zero, n, group, out, stream);
+            if (bits == 4) return launch<F_U4, true>(codes, scale, zero, n, group, out, stream);
+            return launch<F_U2, true>(codes, scale, zero, n, group, out, stream);
+        case 4:  // ternary
+            return launch<F_TER, true>(codes, scale, zero, n, group, out, stream);
         case 1:  // rowwise fp8: group = dim, any multiple of 4
             if ((group & (group - 1)) == 0)
                 return launch<F_FP8, true>(codes, scale, zero, n, group, out, stream);

@@ -51,13 +51,48 @@ __device__ __forceinline__ void store_ef4(float* __restrict__ ef, int64_t i, int
     }
 }
 
-// ============================================================== uniform
-// scale = (max - min) / (2^BITS - 1); code = rint((v - min) / scale);
-// DQ = code*scale + min; ef = v - DQ.
+// Store the codes of a lane's chunk (4 elements from index i) into the
+// payload.  8 bits: one 32-bit word per lane; 4 bits: lanes l and l^1 form
+// one word; 2 bits: lanes 4j..4j+3 form one word.  The lanes of a word hold
+// consecutive chunks, so each word is written by one lane, and only words
+// inside the padded payload are written.
+template <int BITS>
+__device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, int64_t i, int64_t pbytes,
+                                             const uint32_t (&q)[4]) {
+    if constexpr (BITS == 8) {
+        const uint32_t word = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        if (i < pbytes) st_u32(codes + i, word);
+    } else if constexpr (BITS == 4) {
+        const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
+        const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
+        if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(codes + i / 2, half | (other << 16));
+    } else {
+        const uint32_t byte = q[0] | (q[1] << 2) | (q[2] << 4) | (q[3] << 6);
+        const uint32_t word = group_or<4>(byte << (8 * (lane_id() & 3)));
+        if ((lane_id() & 3) == 0 && i / 4 < pbytes) st_u32(codes + i / 4, word);
+    }
+}
 
-template <class G, int BITS, bool EF, bool FULL>
+// Uniform draws in [0, 1) for the 4 elements of a chunk starting at global
+// index g0 (a multiple of 4): the top 24 bits of the Philox4x32-10 block at
+// counter (g0/4, 0) with key = seed, times 2^-24 (exact).
+__device__ __forceinline__ void chunk_draws(uint64_t g0, uint32_t k0, uint32_t k1, float (&u)[4]) {
+    const uint64_t blk = g0 >> 2;
+    const u32x4 r = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u, k0, k1);
+    u[0] = (float)(r.x >> 8) * 0x1p-24f;
+    u[1] = (float)(r.y >> 8) * 0x1p-24f;
+    u[2] = (float)(r.z >> 8) * 0x1p-24f;
+    u[3] = (float)(r.w >> 8) * 0x1p-24f;
+}
+
+// ============================================================== uniform
+// scale = (max - min) / (2^BITS - 1); t = (v - min) / scale; code = rint(t),
+// or (STOCH) floor(t) + (u < frac(t)); DQ = code*scale + min; ef = v - DQ.
+
+template <class G, int BITS, bool EF, bool STOCH, bool FULL>
 __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, float* __restrict__ ef,
-                                               int64_t n, int64_t bk, uint8_t* __restrict__ codes,
+                                               int64_t n, int64_t bk, uint32_t k0, uint32_t k1,
+                                               uint64_t elem_offset, uint8_t* __restrict__ codes,
                                                int64_t pbytes, float* __restrict__ scale,
                                                float* __restrict__ zero, float* lds) {
     constexpr int K = G::K, LPB = G::LPB;
@@ -90,6 +125,10 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int64_t i = base + (int64_t)k * LPB * 4;
+        float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (STOCH) {
+            if (sc != 0.0f && (FULL || i < n)) chunk_draws(elem_offset + (uint64_t)i, k0, k1, u);
+        }
         uint32_t q[4];
         float e[4];
 #pragma unroll
@@ -97,8 +136,15 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
             uint32_t c = 0;
             if (sc != 0.0f) {
                 const float t = (v[k][j] - mn) / sc;
-                const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), (float)L);
-                c = (uint32_t)r;
+                float r;
+                if constexpr (STOCH) {
+                    const float fl = floorf(t);
+                    const float frac = t - fl;
+                    r = fl + (u[j] < frac ? 1.0f : 0.0f);
+                } else {
+                    r = __builtin_rintf(t);
+                }
+                c = (uint32_t)fminf(fmaxf(r, 0.0f), (float)L);
             }
             if (!FULL && i + j >= n) c = 0;
             q[j] = c;
@@ -106,14 +152,7 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
             const float dq = p + mn;
             e[j] = v[k][j] - dq;
         }
-        if constexpr (BITS == 8) {
-            const uint32_t word = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            if (i < pbytes) st_u32(codes + i, word);
-        } else {
-            const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
-            const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
-            if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(codes + i / 2, half | (other << 16));
-        }
+        store_codes4<BITS>(codes, i, pbytes, q);
         if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
     }
     if (bucket_leader<G>()) {
@@ -122,17 +161,19 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
     }
 }
 
-template <class G, int BITS, bool EF>
+template <class G, int BITS, bool EF, bool STOCH>
 __global__ void __launch_bounds__(G::THREADS)
-k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
-              uint8_t* __restrict__ codes, int64_t pbytes, float* __restrict__ scale,
-              float* __restrict__ zero) {
+k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0,
+              uint32_t k1, uint64_t elem_offset, uint8_t* __restrict__ codes, int64_t pbytes,
+              float* __restrict__ scale, float* __restrict__ zero) {
     __shared__ float lds[G::W];
     for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
         if ((bk + 1) * (int64_t)G::B <= n)
-            uniform_bucket<G, BITS, EF, true>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+            uniform_bucket<G, BITS, EF, STOCH, true>(x, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
+                                                      scale, zero, lds);
         else
-            uniform_bucket<G, BITS, EF, false>(x, ef, n, bk, codes, pbytes, scale, zero, lds);
+            uniform_bucket<G, BITS, EF, STOCH, false>(x, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
+                                                       scale, zero, lds);
     }
 }
 
@@ -170,16 +211,14 @@ __device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* 
         uint32_t q[4] = {0u, 0u, 0u, 0u};
         float e[4] = {v[k][0], v[k][1], v[k][2], v[k][3]};
         if (d != 0.0f && (FULL || i < n)) {
-            const uint64_t blk = (elem_offset + (uint64_t)i) >> 2;
-            const u32x4 r = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u, k0, k1);
-            const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+            float u[4];
+            chunk_draws(elem_offset + (uint64_t)i, k0, k1, u);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float t = fabsf(v[k][j]) / d;
                 const float fl = floorf(t);
                 const float frac = t - fl;
-                const float u = (float)(rw[j] >> 8) * 0x1p-24f;
-                uint32_t level = (uint32_t)fl + (u < frac ? 1u : 0u);
+                uint32_t level = (uint32_t)fl + (u[j] < frac ? 1u : 0u);
                 level = level < 7u ? level : 7u;
                 if (!FULL && i + j >= n) level = 0;
                 if (level != 0u) {
@@ -190,9 +229,7 @@ __device__ __forceinline__ void qsgd_bucket(const float* __restrict__ x, float* 
                 }
             }
         }
-        const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
-        const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
-        if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(words + i / 2, half | (other << 16));
+        store_codes4<4>(words, i, pbytes, q);
         if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
     }
     if (bucket_leader<G>()) norm[bk] = nrm;
@@ -209,6 +246,68 @@ k_enc_qsgd(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
             qsgd_bucket<G, EF, true>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
         else
             qsgd_bucket<G, EF, false>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, norm, lds);
+    }
+}
+
+// ============================================================= TernGrad
+// s = max |v| over the bucket; code = (u < |v|/s) ? (v < 0 ? 3 : 1) : 0
+// (bit 0 = nonzero, bit 1 = negative); DQ = 0 or +-s; ef = v - DQ.
+
+template <class G, bool EF, bool FULL>
+__device__ __forceinline__ void ternary_bucket(const float* __restrict__ x, float* __restrict__ ef,
+                                               int64_t n, int64_t bk, uint32_t k0, uint32_t k1,
+                                               uint64_t elem_offset, uint8_t* __restrict__ words,
+                                               int64_t pbytes, float* __restrict__ scale, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+
+    float v[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+
+    float s = 0.0f;  // masked elements load as 0 and do not change the max
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = fmaxf(s, fabsf(v[k][j]));
+    s = group_max<LPB>(s);
+    if constexpr (G::W > 1) s = block_max<G::W>(s, lds);
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 4;
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+        float e[4] = {v[k][0], v[k][1], v[k][2], v[k][3]};
+        if (s != 0.0f && (FULL || i < n)) {
+            float u[4];
+            chunk_draws(elem_offset + (uint64_t)i, k0, k1, u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p = fabsf(v[k][j]) / s;  // a masked element has p = 0: never sent
+                if (u[j] < p) {
+                    const bool neg = v[k][j] < 0.0f;
+                    q[j] = neg ? 3u : 1u;
+                    e[j] = v[k][j] - (neg ? -s : s);
+                }
+            }
+        }
+        store_codes4<2>(words, i, pbytes, q);
+        if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
+    }
+    if (bucket_leader<G>()) scale[bk] = s;
+}
+
+template <class G, bool EF>
+__global__ void __launch_bounds__(G::THREADS)
+k_enc_ternary(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0,
+              uint32_t k1, uint64_t elem_offset, uint8_t* __restrict__ words, int64_t pbytes,
+              float* __restrict__ scale) {
+    __shared__ float lds[G::W];
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        if ((bk + 1) * (int64_t)G::B <= n)
+            ternary_bucket<G, EF, true>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, scale, lds);
+        else
+            ternary_bucket<G, EF, false>(x, ef, n, bk, k0, k1, elem_offset, words, pbytes, scale, lds);
     }
 }
 
@@ -368,20 +467,43 @@ hipError_t with_flag(bool flag, F&& f) {
 }
 
 hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
-                                 void* codes, int64_t payload_bytes, float* scale, float* zero,
-                                 hipStream_t stream) {
+                                 bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                                 int64_t payload_bytes, float* scale, float* zero, hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            return with_flag(stochastic, [&](auto is_stoch) {
+                constexpr bool ST = decltype(is_stoch)::value;
+                if (bits == 8)
+                    hipLaunchKernelGGL((k_enc_uniform<G, 8, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
+                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                else if (bits == 4)
+                    hipLaunchKernelGGL((k_enc_uniform<G, 4, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
+                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                else
+                    hipLaunchKernelGGL((k_enc_uniform<G, 2, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
+                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                return hipGetLastError();
+            });
+        });
+    });
+}
+
+hipError_t launch_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                                 uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,
+                                 float* scale, hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
     return dispatch_bucket<4>(bucket, [&](auto g) {
         using G = decltype(g);
         const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
         return with_flag(ef != nullptr, [&](auto has_ef) {
             constexpr bool EF = decltype(has_ef)::value;
-            if (bits == 8)
-                hipLaunchKernelGGL((k_enc_uniform<G, 8, EF>), grid, block, 0, stream, x, ef, n, nb,
-                                   (uint8_t*)codes, payload_bytes, scale, zero);
-            else
-                hipLaunchKernelGGL((k_enc_uniform<G, 4, EF>), grid, block, 0, stream, x, ef, n, nb,
-                                   (uint8_t*)codes, payload_bytes, scale, zero);
+            hipLaunchKernelGGL((k_enc_ternary<G, EF>), grid, block, 0, stream, x, ef, n, nb, (uint32_t)seed,
+                               (uint32_t)(seed >> 32), elem_offset, (uint8_t*)words, payload_bytes, scale);
             return hipGetLastError();
         });
     });

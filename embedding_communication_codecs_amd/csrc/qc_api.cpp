@@ -41,11 +41,13 @@ int64_t qc_payload_bytes(int32_t fmt, int64_t n, int32_t group, int32_t bits) {
         case QC_UNIFORM:
             if (bits == 8) code_bytes = n;
             else if (bits == 4) code_bytes = 4 * ceil_div(n, 8);
+            else if (bits == 2) code_bytes = 4 * ceil_div(n, 16);
             else return -1;
             break;
         case QC_FP8_ROWWISE: code_bytes = n; break;
         case QC_QSGD: code_bytes = 4 * ceil_div(n, 8); break;
         case QC_SIGN: code_bytes = 4 * ceil_div(n, 32); break;
+        case QC_TERNARY: code_bytes = 4 * ceil_div(n, 16); break;
         default: return -1;
     }
     return ceil_div(code_bytes, 16) * 16;
@@ -62,18 +64,35 @@ const char* qc_status_str(int32_t status) {
     }
 }
 
-int qc_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
-                      void* codes, float* scale, float* zero, qc_stream_t stream) {
-    if (n < 0 || bad_bucket(bucket)) return QC_ERR_ARG;
-    if (bits != 8 && bits != 4) return QC_ERR_UNSUPPORTED;
+namespace {
+
+int encode_uniform_any(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                       bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                       float* scale, float* zero, qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket) || (elem_offset & 3u) != 0) return QC_ERR_ARG;
+    if (bits != 8 && bits != 4 && bits != 2) return QC_ERR_UNSUPPORTED;
     if (n == 0) return QC_OK;
     if (!x || !codes || !scale || !zero) return QC_ERR_ARG;
     if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
     if (misaligned(x) || misaligned(ef) || misaligned(codes) || misaligned(scale) || misaligned(zero))
         return QC_ERR_ALIGN;
-    return launched(qc::launch_encode_uniform(x, ef, n, bucket, bits, codes,
-                                              qc_payload_bytes(QC_UNIFORM, n, bucket, bits), scale,
-                                              zero, hs(stream)));
+    return launched(qc::launch_encode_uniform(x, ef, n, bucket, bits, stochastic, seed, elem_offset,
+                                              codes, qc_payload_bytes(QC_UNIFORM, n, bucket, bits),
+                                              scale, zero, hs(stream)));
+}
+
+}  // namespace
+
+int qc_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                      void* codes, float* scale, float* zero, qc_stream_t stream) {
+    return encode_uniform_any(x, ef, n, bucket, bits, false, 0, 0, codes, scale, zero, stream);
+}
+
+int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                                 uint64_t seed, uint64_t elem_offset, void* codes, float* scale,
+                                 float* zero, qc_stream_t stream) {
+    return encode_uniform_any(x, ef, n, bucket, bits, true, seed, elem_offset, codes, scale, zero,
+                              stream);
 }
 
 int qc_encode_fp8_rowwise(const float* x, int64_t rows, int32_t dim, uint8_t* codes, float* scale,
@@ -103,6 +122,18 @@ int qc_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, int32_t
                                            hs(stream)));
 }
 
+int qc_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                      uint64_t elem_offset, uint32_t* words, float* scale, qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket) || (elem_offset & 3u) != 0) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!x || !words || !scale) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(words) || misaligned(scale)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_ternary(x, ef, n, bucket, seed, elem_offset, words,
+                                              qc_payload_bytes(QC_TERNARY, n, bucket, 2), scale,
+                                              hs(stream)));
+}
+
 int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t bucket,
                    uint32_t* words, float* scale, qc_stream_t stream) {
     if (n < 0 || bad_bucket(bucket) || (xtype != QC_F32 && xtype != QC_BF16)) return QC_ERR_ARG;
@@ -122,7 +153,7 @@ int check_format(int32_t fmt, int64_t n, int32_t group, int32_t bits, const floa
                  bool accumulate_path) {
     switch (fmt) {
         case QC_UNIFORM:
-            if (bits != 8 && bits != 4) return QC_ERR_UNSUPPORTED;
+            if (bits != 8 && bits != 4 && bits != 2) return QC_ERR_UNSUPPORTED;
             if (bad_bucket(group)) return QC_ERR_ARG;
             if (n > 0 && !zero) return QC_ERR_ARG;
             return QC_OK;
@@ -138,6 +169,9 @@ int check_format(int32_t fmt, int64_t n, int32_t group, int32_t bits, const floa
             return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
         case QC_SIGN:
             if (bits != 1) return QC_ERR_UNSUPPORTED;
+            return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
+        case QC_TERNARY:
+            if (bits != 2) return QC_ERR_UNSUPPORTED;
             return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
         default:
             return QC_ERR_UNSUPPORTED;

@@ -44,6 +44,9 @@ __device__ __forceinline__ u32x4 ld_stream_u4(const void* p) {
 __device__ __forceinline__ u32x2 ld_stream_u2(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
+__device__ __forceinline__ uint32_t ld_stream_u32(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 __device__ __forceinline__ uint32_t ld_stream_u16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }

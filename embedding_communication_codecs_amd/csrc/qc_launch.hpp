@@ -19,8 +19,12 @@ inline int log2_exact(int64_t v) {
 }
 
 hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
-                                 void* codes, int64_t payload_bytes, float* scale, float* zero,
-                                 hipStream_t stream);
+                                 bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                                 int64_t payload_bytes, float* scale, float* zero, hipStream_t stream);
+
+hipError_t launch_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                                 uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,
+                                 float* scale, hipStream_t stream);
 
 hipError_t launch_encode_fp8(const float* x, int64_t rows, int32_t dim, uint8_t* codes,
                              int64_t payload_bytes, float* scale, hipStream_t stream);

@@ -29,8 +29,9 @@
  *    (code bytes rounded up to 16).  Encoders write every byte of it;
  *    bytes after the last code are zero.  4-bit codes are packed eight to a
  *    little-endian 32-bit word, element i in bits 4*(i%8)..4*(i%8)+3 of word
- *    i/8; 1-bit codes thirty-two to a word, element i in bit i%32 of word
- *    i/32.  M payloads of one kind are stored back to back, payload w at
+ *    i/8; 2-bit codes sixteen to a word, element i in bits 2*(i%16)..+1 of
+ *    word i/16; 1-bit codes thirty-two to a word, element i in bit i%32 of
+ *    word i/32.  M payloads of one kind are stored back to back, payload w at
  *    byte offset w * qc_payload_bytes(), its per-bucket fp32 statistics at
  *    element offset w * nb of the scale/zero arrays.
  *  - Arithmetic is IEEE fp32 with round-to-nearest-even, no fused
@@ -58,7 +59,7 @@ enum qc_status {
     QC_ERR_LAUNCH = 4        /* the HIP runtime refused the kernel launch */
 };
 
-enum qc_format { QC_UNIFORM = 0, QC_FP8_ROWWISE = 1, QC_QSGD = 2, QC_SIGN = 3 };
+enum qc_format { QC_UNIFORM = 0, QC_FP8_ROWWISE = 1, QC_QSGD = 2, QC_SIGN = 3, QC_TERNARY = 4 };
 enum qc_dtype { QC_F32 = 0, QC_BF16 = 1 };
 
 #define QC_MIN_BUCKET 64
@@ -79,14 +80,34 @@ enum qc_dtype { QC_F32 = 0, QC_BF16 = 1 };
  *
  *   x      fp32[n], read.
  *   ef     fp32[n], read and written in place, or NULL (no feedback).
- *   bits   8 (one byte per code) or 4 (eight codes per word).
+ *   bits   8 (one byte per code), 4 (eight codes per word) or 2 (sixteen
+ *          codes per word; "Quantization for Communication", section
+ *          "Bit-Width Selection", 2-bit).
  *   codes  qc_payload_bytes(QC_UNIFORM, n, bucket, bits) bytes, written.
  *   scale  fp32[nb] written; zero fp32[nb] written.
  * Errors: ARG (NULL x/codes/scale/zero, n < 0, bad bucket), ALIGN,
- *         UNSUPPORTED (bits not 4 or 8).
+ *         UNSUPPORTED (bits not 2, 4 or 8).
  */
 int qc_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
                       void* codes, float* scale, float* zero, qc_stream_t stream);
+
+/*
+ * Uniform quantization with stochastic rounding ("Quantization for
+ * Communication", section "Quantization Schemes", stochastic quantization;
+ * "Gradient quantization for communication", section "Quantization
+ * Schemes"): the same grid, scale and zero as qc_encode_uniform, but with
+ * t = (v - mn) / scale the code is floor(t) + (u < t - floor(t)), capped
+ * at 2^bits - 1, so E[DQ] = v.  u is the QSGD draw of element g =
+ * elem_offset + index (see qc_encode_qsgd).  Payload format and decoding
+ * are those of QC_UNIFORM.
+ *
+ *   bits, x, ef, codes, scale, zero: as for qc_encode_uniform.
+ *   seed, elem_offset: as for qc_encode_qsgd (elem_offset a multiple of 4).
+ * Errors: as qc_encode_uniform, plus ARG for elem_offset % 4 != 0.
+ */
+int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                                 uint64_t seed, uint64_t elem_offset, void* codes, float* scale,
+                                 float* zero, qc_stream_t stream);
 
 /*
  * Rowwise FP8 (OCP E4M3FN) for embedding-lookup payloads: one byte per
@@ -138,6 +159,24 @@ int qc_encode_qsgd(const float* x, float* ef, int64_t n, int32_t bucket, int32_t
                    qc_stream_t stream);
 
 /*
+ * TernGrad: three levels {-1, 0, +1} times a per-bucket scale, with
+ * optional error feedback ("Quantization for Communication", section
+ * "Quantized SGD Algorithms", TernGrad).
+ *
+ * Per bucket, v as above; s = max |v|.  Element v is sent as sign(v) when
+ * u < |v| / s (u the QSGD draw of its global index), else as 0, so
+ * E[DQ] = v.  Codes are 2 bits: bit 0 = nonzero, bit 1 = negative (0, 1 =
+ * +s, 3 = -s).  All codes are 0 when s == 0.  With ef: ef = v - DQ.
+ *
+ *   x, ef, seed, elem_offset: as for qc_encode_qsgd.
+ *   words  qc_payload_bytes(QC_TERNARY, n, bucket, 2) bytes, written.
+ *   scale  fp32[nb] (the per-bucket s), written.
+ * Errors: ARG (NULL pointer, n < 0, bad bucket, elem_offset % 4 != 0), ALIGN.
+ */
+int qc_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
+                      uint64_t elem_offset, uint32_t* words, float* scale, qc_stream_t stream);
+
+/*
  * 1-bit sign quantization with a per-bucket scale and optional error
  * feedback ("Quantization for Communication", sections "Bit-Width
  * Selection" and "Quantized SGD Algorithms", SignSGD; "Gradient
@@ -162,10 +201,11 @@ int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t b
  * Decode one payload to fp32 (receive side: "Quantized Communication for
  * Distributed Training", section "Where Quantization Sits").
  *
- *   fmt    QC_UNIFORM: bits 8 or 4, scale and zero per bucket of `group`;
+ *   fmt    QC_UNIFORM: bits 8, 4 or 2, scale and zero per bucket of `group`;
  *          QC_FP8_ROWWISE: group = dim, scale per row, zero unused;
  *          QC_QSGD: bits = 16 (levels), scale = the norm array, zero unused;
- *          QC_SIGN: bits = 1, scale per bucket, zero unused.
+ *          QC_SIGN: bits = 1, scale per bucket, zero unused;
+ *          QC_TERNARY: bits = 2, scale per bucket, zero unused.
  *   codes  the payload, read.   out  fp32[n], written.
  * DQ is the formula stated for the matching encoder.
  * Errors: ARG (NULL pointer, n < 0, bad group, n % dim != 0 for FP8),
@@ -220,7 +260,8 @@ int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_
 
 /*
  * Bytes of one payload of n elements: the code bytes (n for INT8/FP8,
- * 4*ceil(n/8) for 4-bit formats, 4*ceil(n/32) for sign) rounded up to 16.
+ * 4*ceil(n/8) for 4-bit formats, 4*ceil(n/16) for 2-bit formats,
+ * 4*ceil(n/32) for sign) rounded up to 16.
  * `group` is accepted for symmetry and does not change the size.  Returns
  * -1 for an unknown format/bits or n < 0.
  */

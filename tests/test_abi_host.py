@@ -47,6 +47,8 @@ def test_payload_bytes_matches_oracle(qc, ora):
     for n in (0, 1, 3, 4, 15, 16, 17, 31, 32, 33, 127, 128, 129, 1000, 65536, 10**9):
         assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 8) == ora.payload_bytes(ora.UNIFORM, n, 8)
         assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 4) == ora.payload_bytes(ora.UNIFORM, n, 4)
+        assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 2) == ora.payload_bytes(ora.UNIFORM, n, 2)
+        assert qc.qc_payload_bytes(qc.QC_TERNARY, n, 64, 2) == ora.payload_bytes(ora.TERNARY, n, 2)
         assert qc.qc_payload_bytes(qc.QC_FP8_ROWWISE, n, 4, 8) == ora.payload_bytes(ora.FP8_ROWWISE, n)
         assert qc.qc_payload_bytes(qc.QC_QSGD, n, 512, 16) == ora.payload_bytes(ora.QSGD, n, 4)
         assert qc.qc_payload_bytes(qc.QC_SIGN, n, 4096, 1) == ora.payload_bytes(ora.SIGN, n, 1)
@@ -78,7 +80,7 @@ def test_encode_uniform_errors(qc):
     assert call(qc, f, A, A, -1, 256, 8, A, A, A, None) == qc.QC_ERR_ARG
     for bad in (0, 32, 100, 96, 131072, -64):
         assert call(qc, f, A, A, 1000, bad, 8, A, A, A, None) == qc.QC_ERR_ARG, bad
-    for bits in (0, 1, 2, 3, 5, 16):
+    for bits in (0, 1, 3, 5, 16):
         assert call(qc, f, A, A, 1000, 256, bits, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
     assert call(qc, f, A, A, 1000, 256, 8, NULL, A, A, None) == qc.QC_ERR_ARG
     assert call(qc, f, A, A, 1000, 256, 8, A, NULL, A, None) == qc.QC_ERR_ARG
@@ -89,6 +91,42 @@ def test_encode_uniform_errors(qc):
         assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
     # empty input is a valid no-op, even with NULL buffers
     assert call(qc, f, NULL, NULL, 0, 256, 8, NULL, NULL, NULL, None) == qc.QC_OK
+
+
+def test_encode_uniform_stochastic_errors(qc):
+    f = "qc_encode_uniform_stochastic"
+    ok = (A, A, 1000, 256, 2, 7, 8, A, A, A, None)
+    assert call(qc, f, *ok[:6], 6, *ok[7:]) == qc.QC_ERR_ARG  # offset % 4
+    assert call(qc, f, NULL, *ok[1:]) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 192, 2, 7, 8, A, A, A, None) == qc.QC_ERR_ARG
+    for bits in (0, 1, 3, 16):
+        assert call(qc, f, A, A, 1000, 256, bits, 7, 8, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    for pos in (7, 8, 9):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    for pos in (0, 1, 7, 8, 9):
+        args = list(ok)
+        args[pos] = MIS
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    assert call(qc, f, NULL, NULL, 0, 256, 4, 7, 8, NULL, NULL, NULL, None) == qc.QC_OK
+
+
+def test_encode_ternary_errors(qc):
+    f = "qc_encode_ternary"
+    ok = (A, A, 1000, 512, 3, 4, A, A, None)
+    assert call(qc, f, *ok[:5], 2, *ok[6:]) == qc.QC_ERR_ARG  # offset % 4
+    assert call(qc, f, A, A, -5, 512, 3, 4, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 48, 3, 4, A, A, None) == qc.QC_ERR_ARG
+    for pos in (0, 6, 7):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    for pos in (0, 1, 6, 7):
+        args = list(ok)
+        args[pos] = MIS
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    assert call(qc, f, NULL, NULL, 0, 512, 3, 4, NULL, NULL, None) == qc.QC_OK
 
 
 def test_encode_fp8_errors(qc):
@@ -127,7 +165,10 @@ def test_encode_sign_errors(qc):
 def test_decode_errors(qc):
     f = "qc_decode"
     assert call(qc, f, 7, A, A, A, 100, 64, 8, A, None) == qc.QC_ERR_UNSUPPORTED
-    assert call(qc, f, qc.QC_UNIFORM, A, A, A, 100, 64, 2, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_UNIFORM, A, A, A, 100, 64, 3, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_TERNARY, A, A, NULL, 100, 64, 4, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_TERNARY, A, A, NULL, 100, 96, 2, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, qc.QC_TERNARY, A, MIS, NULL, 100, 64, 2, A, None) == qc.QC_ERR_ALIGN
     assert call(qc, f, qc.QC_UNIFORM, A, A, NULL, 100, 64, 8, A, None) == qc.QC_ERR_ARG  # zero needed
     assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 100, 128, 8, A, None) == qc.QC_ERR_ARG  # n % dim
     assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 128, 6, 8, A, None) == qc.QC_ERR_UNSUPPORTED
@@ -145,6 +186,8 @@ def test_dequant_accumulate_errors(qc):
     assert call(qc, f, U, A, A, A, 65536, 100, 64, 8, A, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ARG
     assert call(qc, f, U, A, A, A, 4, 100, 64, 8, A, 0, A, NULL, NULL, None) == qc.QC_ERR_ARG
     assert call(qc, f, qc.QC_SIGN, A, A, NULL, 4, 100, 64, 1, A, 0, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, qc.QC_TERNARY, A, A, NULL, 4, 100, 64, 2, A, 0, A, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, U, A, A, A, 4, 100, 64, 3, A, 0, NULL, NULL, NULL, None) == qc.QC_ERR_UNSUPPORTED
     assert call(qc, f, qc.QC_FP8_ROWWISE, A, A, NULL, 4, 96 * 3, 96, 8, A, 0, NULL, NULL, NULL,
                 None) == qc.QC_ERR_UNSUPPORTED  # rows for accumulation: power-of-two dims
     assert call(qc, f, U, A, A, A, 4, 100, 64, 8, MIS, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ALIGN

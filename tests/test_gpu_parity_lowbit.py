@@ -1,0 +1,311 @@
+"""GPU parity for the low-bit codecs: 2-bit uniform, uniform quantization
+with stochastic rounding (8, 4 and 2 bits) and TernGrad, each called
+through the C ABI and compared bit for bit with the CPU oracle on the same
+seeded inputs (codes, scales, zero points, residuals, decoded values and
+worker sums), at sizes spanning several tiles with ragged tails, plus the
+degenerate buckets of each method."""
+import numpy as np
+import pytest
+
+from embedding_communication_codecs_amd import synth
+from gpu_util import Out, bits_equal, dev, dev_ef, first_diff, need_gpu, out_f32
+
+pytestmark = pytest.mark.gpu
+
+BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536]
+
+
+@pytest.fixture(scope="module")
+def qc():
+    return need_gpu()
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def run_uniform(qc, x, ef, bucket, bits, stochastic=False, seed=0, offset=0):
+    n = x.size
+    nb = qc.nbuckets(n, bucket)
+    codes = Out(qc.payload_bytes(qc.QC_UNIFORM, n, bucket, bits))
+    scale, zero = out_f32(nb), out_f32(nb)
+    e = None if ef is None else ef.t
+    if stochastic:
+        qc.qc_encode_uniform_stochastic(dev(x), e, n, bucket, bits, seed, offset, codes.t, scale.t, zero.t)
+    else:
+        qc.qc_encode_uniform(dev(x), e, n, bucket, bits, codes.t, scale.t, zero.t)
+    sync()
+    return codes, scale, zero
+
+
+def run_ternary(qc, x, ef, bucket, seed, offset):
+    n = x.size
+    words = Out(qc.payload_bytes(qc.QC_TERNARY, n, bucket, 2))
+    scale = out_f32(qc.nbuckets(n, bucket))
+    qc.qc_encode_ternary(dev(x), None if ef is None else ef.t, n, bucket, seed, offset, words.t, scale.t)
+    sync()
+    return words, scale
+
+
+def decode(qc, fmt, codes, scale, zero, n, bucket, bits):
+    out = out_f32(n)
+    qc.qc_decode(fmt, codes.t, scale.t, None if zero is None else zero.t, n, bucket, bits, out.t)
+    sync()
+    return out.f32()
+
+
+# ============================================================ 2-bit uniform
+
+
+@pytest.mark.parametrize("bucket", BUCKETS)
+def test_int2_parity_ef_steps(qc, ora, bucket):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(3):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=7000 * bucket + step)
+        codes, scale, zero = run_uniform(qc, g, ef_d, bucket, 2)
+        p, s, z = ora.encode_uniform(g, ef_h, bucket, 2)
+        assert bits_equal(codes.host(), p), (step, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(zero.f32(), z), first_diff(zero.f32(), z)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    got = decode(qc, qc.QC_UNIFORM, codes, scale, zero, n, bucket, 2)
+    want = ora.decode_uniform(p, s, z, n, bucket, 2)
+    assert bits_equal(got, want), first_diff(got, want)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 1000, 4096 * 5 + 3])
+def test_int2_ragged_no_ef(qc, ora, n):
+    x = synth.host_normal(n, 1.0, seed=n + 5)
+    codes, scale, zero = run_uniform(qc, x, None, 256, 2)
+    p, s, z = ora.encode_uniform(x, None, 256, 2)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+    got = decode(qc, qc.QC_UNIFORM, codes, scale, zero, n, 256, 2)
+    assert bits_equal(got, ora.decode_uniform(p, s, z, n, 256, 2))
+
+
+# ============================================ uniform, stochastic rounding
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("bucket", BUCKETS)
+def test_stochastic_uniform_parity_ef_steps(qc, ora, bucket, bits):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(2):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=9100 * bucket + 10 * bits + step)
+        seed = 0x53544F4300000000 + 31 * step + bits
+        codes, scale, zero = run_uniform(qc, g, ef_d, bucket, bits, True, seed, 0)
+        p, s, z = ora.encode_uniform_stochastic(g, ef_h, bucket, bits, seed, 0)
+        assert bits_equal(codes.host(), p), (step, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(zero.f32(), z), first_diff(zero.f32(), z)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    got = decode(qc, qc.QC_UNIFORM, codes, scale, zero, n, bucket, bits)
+    want = ora.decode_uniform(p, s, z, n, bucket, bits)
+    assert bits_equal(got, want), first_diff(got, want)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("offset", [0, 4, 4 * 987654321, 2**40 + 4])
+@pytest.mark.parametrize("n", [1, 5, 511, 513, 2000])
+def test_stochastic_uniform_offsets_and_tails(qc, ora, n, offset, bits):
+    x = synth.host_laplace(n, 1e-2, seed=n + 17)
+    codes, scale, zero = run_uniform(qc, x, None, 512, bits, True, 0xDEADBEEF12345678, offset)
+    p, s, z = ora.encode_uniform_stochastic(x, None, 512, bits, 0xDEADBEEF12345678, offset)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_low_bit_uniform_special_values(qc, ora, bits):
+    """Constant buckets, signed zeros, subnormals, values on the grid and
+    near ties, and a huge range, for both rounding rules."""
+    B = 64
+    L = (1 << bits) - 1
+    rows = [
+        np.full(B, 0.5, np.float32),
+        np.array([-0.0] * 32 + [0.0] * 32, np.float32),
+        np.array([1e-45, -1e-45, 3e-39, -2e-39] * 16, np.float32),
+        np.linspace(-1, 1, B).astype(np.float32),
+        (np.arange(B, dtype=np.float32) % (L + 1)) * np.float32(1.0 / L),   # on grid
+        ((np.arange(B, dtype=np.float32) % (L + 1)) + np.float32(0.5)) * np.float32(1.0 / L),
+        np.array([1e30, -1e30] + [0.0] * 62, np.float32),
+    ]
+    x = np.concatenate(rows)
+    for stochastic in (False, True):
+        ef_h = synth.host_normal(x.size, 1e-7, seed=40 + bits).astype(np.float32)
+        ef_d = dev_ef(ef_h)
+        codes, scale, zero = run_uniform(qc, x, ef_d, B, bits, stochastic, 4242, 8)
+        if stochastic:
+            p, s, z = ora.encode_uniform_stochastic(x, ef_h, B, bits, 4242, 8)
+        else:
+            p, s, z = ora.encode_uniform(x, ef_h, B, bits)
+        assert bits_equal(codes.host(), p), (stochastic, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+
+
+def test_stochastic_uniform_seed_and_offset_change_codes(qc, ora):
+    """Sanity on the randomness itself: a different seed or offset gives
+    different codes (and the oracle agrees on each)."""
+    n, B = 8192, 1024
+    x = synth.host_normal(n, 1.0, seed=3)
+    runs = []
+    for seed, off in ((1, 0), (2, 0), (1, 4096)):
+        codes, _, _ = run_uniform(qc, x, None, B, 4, True, seed, off)
+        p, _, _ = ora.encode_uniform_stochastic(x, None, B, 4, seed, off)
+        assert bits_equal(codes.host(), p)
+        runs.append(codes.host())
+    assert not np.array_equal(runs[0], runs[1])
+    assert not np.array_equal(runs[0], runs[2])
+
+
+# =============================================================== TernGrad
+
+
+@pytest.mark.parametrize("bucket", BUCKETS)
+def test_ternary_parity_ef_steps(qc, ora, bucket):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(3):
+        g = synth.host_laplace(n, 1e-4, seed=8100 + step + bucket)
+        seed = 0x5445524E00000000 + step
+        words, scale = run_ternary(qc, g, ef_d, bucket, seed, 0)
+        p, s = ora.encode_ternary(g, ef_h, bucket, seed, 0)
+        assert bits_equal(words.host(), p), (step, first_diff(words.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    got = decode(qc, qc.QC_TERNARY, words, scale, None, n, bucket, 2)
+    want = ora.decode_ternary(p, s, n, bucket)
+    assert bits_equal(got, want), first_diff(got, want)
+
+
+@pytest.mark.parametrize("offset", [0, 4, 4 * 123456789, 2**40])
+@pytest.mark.parametrize("n", [1, 5, 15, 16, 17, 511, 513, 2000])
+def test_ternary_offsets_and_tails(qc, ora, n, offset):
+    x = synth.host_laplace(n, 1e-4, seed=n + 23)
+    words, scale = run_ternary(qc, x, None, 512, 0xFEEDFACECAFEBEEF, offset)
+    p, s = ora.encode_ternary(x, None, 512, 0xFEEDFACECAFEBEEF, offset)
+    assert bits_equal(words.host(), p), first_diff(words.host(), p)
+    assert bits_equal(scale.f32(), s)
+    got = decode(qc, qc.QC_TERNARY, words, scale, None, n, 512, 2)
+    assert bits_equal(got, ora.decode_ternary(p, s, n, 512))
+
+
+def test_ternary_special_values(qc, ora):
+    B = 64
+    x = np.concatenate([
+        np.zeros(B, np.float32),                                    # s == 0: all codes 0
+        np.array([-3.0] + [0.0] * 63, np.float32),                  # the max is always sent
+        np.array([2.0, -2.0, 2.0, -2.0] * 16, np.float32),          # |v| == s everywhere
+        np.array([1e-45] * 64, np.float32),                         # subnormal scale
+        np.array([-0.0] * 32 + [1e-3] * 32, np.float32),
+        np.array([1e30, -1e-30] + [0.0] * 62, np.float32),
+    ])
+    ef_h = np.zeros(x.size, np.float32)
+    ef_d = dev_ef(ef_h)
+    words, scale = run_ternary(qc, x, ef_d, B, 99, 0)
+    p, s = ora.encode_ternary(x, ef_h, B, 99, 0)
+    assert bits_equal(words.host(), p) and bits_equal(scale.f32(), s)
+    assert bits_equal(ef_d.f32(), ef_h)
+
+
+# ============================================================= accumulate
+
+
+def make_payloads(ora, fmt, m, n, group, seed):
+    parts, sc, ze = [], [], []
+    for w in range(m):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=seed + w)
+        if fmt == "u2":
+            p, s, z = ora.encode_uniform(g, None, group, 2)
+            ze.append(z)
+        elif fmt == "u2s":
+            p, s, z = ora.encode_uniform_stochastic(g, None, group, 2, seed + w, 4 * w)
+            ze.append(z)
+        else:
+            p, s = ora.encode_ternary(g, None, group, seed + w, 0)
+        parts.append(p)
+        sc.append(s)
+    zero = np.concatenate(ze) if ze else None
+    return np.concatenate(parts), np.concatenate(sc), zero
+
+
+CODE = {"u2": 0, "u2s": 0, "ter": 4}
+
+
+@pytest.mark.parametrize("fmt,group", [("u2", 64), ("u2", 256), ("u2", 2048), ("u2", 8192), ("u2s", 512),
+                                       ("ter", 64), ("ter", 512), ("ter", 4096)])
+@pytest.mark.parametrize("m", [1, 3, 16, 65, 130])
+def test_dequant_accumulate_low_bit(qc, ora, fmt, group, m):
+    n = 3 * group + 37
+    payloads, scale, zero = make_payloads(ora, fmt, m, n, group, seed=600 + m)
+    code = CODE[fmt]
+    want = ora.dequant_accumulate(code, payloads, scale, zero, m, n, group, 2)
+    acc = out_f32(n)
+    zd = None if zero is None else dev(zero)
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), zd, m, n, group, 2, acc.t, False)
+    sync()
+    assert bits_equal(acc.f32(), want), first_diff(acc.f32(), want)
+    start = synth.host_normal(n, 1e-3, seed=78)
+    acc.t.copy_(dev(start))
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), zd, m, n, group, 2, acc.t, True)
+    sync()
+    want2 = ora.dequant_accumulate(code, payloads, scale, zero, m, n, group, 2, acc=start)
+    assert bits_equal(acc.f32(), want2), first_diff(acc.f32(), want2)
+
+
+@pytest.mark.parametrize("group", [64, 512, 2048, 8192])
+def test_dequant_accumulate_requant_int2(qc, ora, group):
+    m, n = 6, 3 * group + 21
+    payloads, scale, zero = make_payloads(ora, "u2", m, n, group, seed=9200)
+    acc = out_f32(n)
+    nb = qc.nbuckets(n, group)
+    rq = Out(qc.payload_bytes(qc.QC_UNIFORM, n, group, 2))
+    rqs, rqz = out_f32(nb), out_f32(nb)
+    qc.qc_dequant_accumulate(0, dev(payloads), dev(scale), dev(zero), m, n, group, 2, acc.t, False,
+                             rq.t, rqs.t, rqz.t)
+    sync()
+    want = ora.dequant_accumulate(0, payloads, scale, zero, m, n, group, 2)
+    assert bits_equal(acc.f32(), want)
+    p, s, z = ora.encode_uniform(want, None, group, 2)
+    assert bits_equal(rq.host(), p), first_diff(rq.host(), p)
+    assert bits_equal(rqs.f32(), s) and bits_equal(rqz.f32(), z)
+
+
+# ========================================================== random shapes
+
+
+def test_random_shapes_low_bit(qc, ora):
+    """Seeded sweep over n, bucket, bits, seed, offset and EF state."""
+    rng = np.random.default_rng(77)
+    for trial in range(30):
+        n = int(rng.integers(1, 20000))
+        bucket = int(2 ** rng.integers(6, 14))
+        bits = int(rng.choice([8, 4, 2]))
+        sigma = float(10.0 ** rng.integers(-6, 2))
+        x = synth.host_outlier_grad(n, sigma, 0.02, 50.0, seed=500 + trial)
+        seed = int(rng.integers(0, 2**63))
+        off = 4 * int(rng.integers(0, 2**40))
+        ef_h = synth.host_normal(n, sigma * 0.1, seed=5000 + trial)
+        ef_d = dev_ef(ef_h)
+        codes, scale, zero = run_uniform(qc, x, ef_d, bucket, bits, True, seed, off)
+        p, s, z = ora.encode_uniform_stochastic(x, ef_h, bucket, bits, seed, off)
+        assert bits_equal(codes.host(), p), (trial, n, bucket, bits)
+        assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z) and bits_equal(ef_d.f32(), ef_h)
+        ef_h = synth.host_normal(n, sigma * 0.1, seed=6000 + trial)
+        ef_d = dev_ef(ef_h)
+        words, ts = run_ternary(qc, x, ef_d, bucket, seed, off)
+        p, s = ora.encode_ternary(x, ef_h, bucket, seed, off)
+        assert bits_equal(words.host(), p) and bits_equal(ts.f32(), s), (trial, n, bucket)
+        assert bits_equal(ef_d.f32(), ef_h)
+        codes, scale, zero = run_uniform(qc, x, None, bucket, 2)
+        p, s, z = ora.encode_uniform(x, None, bucket, 2)
+        assert bits_equal(codes.host(), p), (trial, n, bucket)
