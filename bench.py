@@ -11,6 +11,14 @@ synthetic input, every op at its full workload size:
   dequantize-accumulate of 64 INT8 payloads of 2^26 (buckets of 2,048)
     with the sum requantized to INT8 in the same pass
 
+Beside the step, in a timed region of its own that `value` does not
+include, the low-bit extensions run on the same 1e9-element gradient:
+2-bit uniform and 4-bit stochastic uniform (buckets of 512, error
+feedback), TernGrad (buckets of 512, error feedback), their decoders, and
+the receive-side sum of 64 workers' TernGrad and 2-bit payloads of 2^26
+(the 2-bit sum requantized to 2 bits in the same pass).  They are reported
+under `extensions`, in the same form as `ops`.
+
 Encoders run first and decoders later in the step, so a decoder never
 reads a payload that is still in the 256 MB last-level cache.  Inputs are
 generated on the GPU (seeded) before timing; the timed region only runs
@@ -46,6 +54,9 @@ C2_ROWS, C2_DIM = 1_000_000, 128
 C3_N, C3_B = 1_000_000_000, 512
 C4_N, C4_B, C4_M = 1 << 28, 4096, 16
 C5_M, C5_N, C5_B = 64, 1 << 26, 2048
+# low-bit extensions: on the QSGD gradient, and 64 workers' payloads like C5
+X_N, X_B = C3_N, 512
+X_M, X_AN, X_AB = 64, 1 << 26, 2048
 
 
 def source_hash() -> str:
@@ -76,17 +87,34 @@ def op_bytes():
         "sign_vote": (C4_M * sign_pb, C4_M * sign_pb + sign_pb),
         "sign_dec": (4 * C4_N, sign_pb + 4 * nb4 + 4 * C4_N),
         "acc_requant": (4 * C5_M * C5_N, C5_M * (C5_N + 8 * nb5) + 4 * C5_N + C5_N + 8 * nb5),
+        **ext_bytes(),
+    }
+
+
+def ext_bytes():
+    nbx = -(-X_N // X_B)
+    nba = X_AN // X_AB
+    return {
+        # x + ef read, ef written, 2-bit codes + scale/zero written
+        "int2_enc": (4 * X_N, 12 * X_N + X_N // 4 + 8 * nbx),
+        "stoch4_enc": (4 * X_N, 12 * X_N + X_N // 2 + 8 * nbx),
+        "tern_enc": (4 * X_N, 12 * X_N + X_N // 4 + 4 * nbx),
+        "int2_dec": (4 * X_N, X_N // 4 + 8 * nbx + 4 * X_N),
+        "tern_dec": (4 * X_N, X_N // 4 + 4 * nbx + 4 * X_N),
+        "acc_tern": (4 * X_M * X_AN, X_M * (X_AN // 4 + 4 * nba) + 4 * X_AN),
+        "acc_int2_requant": (4 * X_M * X_AN, X_M * (X_AN // 4 + 8 * nba) + 4 * X_AN + X_AN // 4 + 8 * nba),
     }
 
 
 ORDER = ["uniform_enc", "qsgd_enc", "fp8_enc", "sign_enc", "acc_requant", "sign_vote", "qsgd_dec",
          "fp8_dec", "sign_dec", "uniform_dec"]
+EXT_ORDER = ["int2_enc", "stoch4_enc", "tern_enc", "acc_tern", "acc_int2_requant", "int2_dec", "tern_dec"]
 
 
 # ------------------------------------------------------------- GPU setup
 
 
-def setup(qc, synth, torch):
+def setup(qc, synth, torch, ext):
     dev = torch.device("cuda")
     st = {}
     U8, F32 = torch.uint8, torch.float32
@@ -136,8 +164,41 @@ def setup(qc, synth, torch):
     st["c5_rq"] = empty(pb5)
     st["c5_rqs"] = torch.empty(nb5, dtype=F32, device=dev)
     st["c5_rqz"] = torch.empty(nb5, dtype=F32, device=dev)
+    if ext:
+        setup_ext(qc, synth, torch, st, empty)
     torch.cuda.synchronize()
     return st
+
+
+def setup_ext(qc, synth, torch, st, empty):
+    dev, F32 = torch.device("cuda"), torch.float32
+    nbx = -(-X_N // X_B)
+    st["x_ef"] = torch.zeros(X_N, dtype=F32, device=dev)
+    st["x_i2"] = empty(qc.payload_bytes(qc.QC_UNIFORM, X_N, X_B, 2))
+    st["x_s4"] = empty(qc.payload_bytes(qc.QC_UNIFORM, X_N, X_B, 4))
+    st["x_t"] = empty(qc.payload_bytes(qc.QC_TERNARY, X_N, X_B, 2))
+    for k in ("x_i2s", "x_i2z", "x_s4s", "x_s4z", "x_ts"):
+        st[k] = torch.empty(nbx, dtype=F32, device=dev)
+    # 64 workers' TernGrad and 2-bit payloads of outlier gradients
+    nba = X_AN // X_AB
+    pbt = qc.payload_bytes(qc.QC_TERNARY, X_AN, X_AB, 2)
+    pbi = qc.payload_bytes(qc.QC_UNIFORM, X_AN, X_AB, 2)
+    st["xa_t"], st["xa_i2"] = empty(X_M * pbt), empty(X_M * pbi)
+    st["xa_ts"] = torch.empty(X_M * nba, dtype=F32, device=dev)
+    st["xa_i2s"] = torch.empty(X_M * nba, dtype=F32, device=dev)
+    st["xa_i2z"] = torch.empty(X_M * nba, dtype=F32, device=dev)
+    for w in range(X_M):
+        g = synth.device_outlier_grad(X_AN, 1e-3, 0.01, 100.0, 6000 + w, dev)
+        sl = slice(w * nba, (w + 1) * nba)
+        qc.qc_encode_ternary(g, None, X_AN, X_AB, 0x5445524E + w, 0, st["xa_t"][w * pbt:(w + 1) * pbt],
+                             st["xa_ts"][sl])
+        qc.qc_encode_uniform(g, None, X_AN, X_AB, 2, st["xa_i2"][w * pbi:(w + 1) * pbi], st["xa_i2s"][sl],
+                             st["xa_i2z"][sl])
+        del g
+    st["xa_acc"] = torch.empty(X_AN, dtype=F32, device=dev)
+    st["xa_rq"] = empty(pbi)
+    st["xa_rqs"] = torch.empty(nba, dtype=F32, device=dev)
+    st["xa_rqz"] = torch.empty(nba, dtype=F32, device=dev)
 
 
 def make_ops(qc, st):
@@ -162,6 +223,21 @@ def make_ops(qc, st):
         "acc_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["c5_arena"], s["c5_scale"],
                                                         s["c5_zero"], C5_M, C5_N, C5_B, 8, s["c5_acc"], False,
                                                         s["c5_rq"], s["c5_rqs"], s["c5_rqz"]),
+        # extensions (present when setup_ext ran)
+        "int2_enc": lambda: qc.qc_encode_uniform(s["c3_x"], s["x_ef"], X_N, X_B, 2, s["x_i2"], s["x_i2s"],
+                                                 s["x_i2z"]),
+        "stoch4_enc": lambda: qc.qc_encode_uniform_stochastic(s["c3_x"], s["x_ef"], X_N, X_B, 4, 0x53544F43, 0,
+                                                              s["x_s4"], s["x_s4s"], s["x_s4z"]),
+        "tern_enc": lambda: qc.qc_encode_ternary(s["c3_x"], s["x_ef"], X_N, X_B, 0x5445524E, 0, s["x_t"],
+                                                 s["x_ts"]),
+        "int2_dec": lambda: qc.qc_decode(qc.QC_UNIFORM, s["x_i2"], s["x_i2s"], s["x_i2z"], X_N, X_B, 2,
+                                         s["c3_out"]),
+        "tern_dec": lambda: qc.qc_decode(qc.QC_TERNARY, s["x_t"], s["x_ts"], None, X_N, X_B, 2, s["c3_out"]),
+        "acc_tern": lambda: qc.qc_dequant_accumulate(qc.QC_TERNARY, s["xa_t"], s["xa_ts"], None, X_M, X_AN,
+                                                     X_AB, 2, s["xa_acc"], False),
+        "acc_int2_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["xa_i2"], s["xa_i2s"], s["xa_i2z"],
+                                                             X_M, X_AN, X_AB, 2, s["xa_acc"], False, s["xa_rq"],
+                                                             s["xa_rqs"], s["xa_rqz"]),
     }
 
 
@@ -291,13 +367,53 @@ def load_traffic(kernel_op):
     return None if e is None else e.get("hbm_bytes")
 
 
+def time_ops(torch, ops, names, sizes, steps, warmup, extra):
+    """Run `names` in order, `warmup` untimed passes then `steps` timed
+    ones, with HIP events around every launch on the launching stream.
+    Returns (wall ms per pass, per-op figures)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for o in names:
+            ops[o]()
+        if extra:
+            extra()
+    torch.cuda.synchronize()
+    ev = {o: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] for o in names}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        for o in names:
+            a, b = ev[o][k]
+            a.record(stream)
+            ops[o]()
+            b.record(stream)
+        if extra:
+            extra()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per_op = {}
+    for o in names:
+        ms = sum(a.elapsed_time(b) for a, b in ev[o]) / steps
+        inb, hbm = sizes[o]
+        per_op[o] = {
+            "ms": round(ms, 4),
+            "input_GBps": round(inb / (ms * 1e-3) / 1e9, 1),
+            "hbm_GBps": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": hbm,
+        }
+    return wall_ms, per_op
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ops", default=",".join(ORDER), help="comma-separated subset of ops to run")
+    ap.add_argument("--ops", default=",".join(ORDER + EXT_ORDER), help="comma-separated subset of ops to run")
+    ap.add_argument("--no-extensions", action="store_true", help="skip the low-bit extension ops")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy each step (counter calibration)")
     ap.add_argument("--calibrate", action="store_true",
@@ -321,53 +437,29 @@ def main():
     if args.calibrate:
         print(json.dumps({"calibration": calibrate(torch)}))
         return
-    names = [o for o in ORDER if o in args.ops.split(",")]
-    print(f"[bench] generating inputs for {names}", file=sys.stderr, flush=True)
-    st = setup(qc, synth, torch)
+    wanted = args.ops.split(",")
+    names = [o for o in ORDER if o in wanted]
+    ext_names = [] if args.no_extensions else [o for o in EXT_ORDER if o in wanted]
+    print(f"[bench] generating inputs for {names + ext_names}", file=sys.stderr, flush=True)
+    st = setup(qc, synth, torch, bool(ext_names))
     ops = make_ops(qc, st)
+    extra = None
     if args.copy_calibration:
         cal_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         cal_dst = torch.empty_like(cal_src)
+        extra = lambda: cal_dst.copy_(cal_src)  # noqa: E731
     sizes = op_bytes()
 
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        for o in names:
-            ops[o]()
-        if args.copy_calibration:
-            cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    ev = {o: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for o in names}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        for o in names:
-            a, b = ev[o][k]
-            a.record(stream)
-            ops[o]()
-            b.record(stream)
-        if args.copy_calibration:
-            cal_dst.copy_(cal_src)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    per_op = {}
-    total_in = 0
-    for o in names:
-        ms = sum(a.elapsed_time(b) for a, b in ev[o]) / args.steps
-        inb, hbm = sizes[o]
-        total_in += inb
-        per_op[o] = {
-            "ms": round(ms, 4),
-            "input_GBps": round(inb / (ms * 1e-3) / 1e9, 1),
-            "hbm_GBps": round(hbm / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "algorithmic_bytes": hbm,
-        }
+    if not names:
+        print("bench.py: --ops names none of the suite's ops " + ",".join(ORDER), file=sys.stderr)
+        sys.exit(2)
+    ms_per_step, per_op = time_ops(torch, ops, names, sizes, args.steps, args.warmup, extra)
+    print(f"[bench] suite timed ({args.steps} steps after {args.warmup} warmup)", file=sys.stderr, flush=True)
+    ext = None
+    if ext_names:
+        ext_ms, ext = time_ops(torch, ops, ext_names, sizes, args.steps, args.warmup, None)
+        print(f"[bench] extensions timed ({ext_ms:.3f} ms per pass)", file=sys.stderr, flush=True)
+    total_in = sum(sizes[o][0] for o in names)
     dom = max(names, key=lambda o: per_op[o]["ms"])
     achieved = per_op[dom]["hbm_GBps"]
     traffic = load_traffic(dom)
@@ -391,6 +483,8 @@ def main():
             "qsgd": f"{C3_N} fp32, bucket {C3_B}, s=16, EF",
             "sign": f"{C4_N} bf16, bucket {C4_B}, EF; vote M={C4_M}",
             "accumulate": f"M={C5_M} x {C5_N} INT8, bucket {C5_B}, fused INT8 requant",
+            "extensions": (f"outside the step: {X_N} fp32, bucket {X_B}, EF: INT2, stochastic INT4, TernGrad "
+                           f"+ decode; M={X_M} x {X_AN}, bucket {X_AB}: TernGrad sum, INT2 sum + INT2 requant"),
         },
         "hbm_frac_step": round(sum(sizes[o][1] for o in names) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {
@@ -404,6 +498,8 @@ def main():
         },
         "ops": per_op,
     }
+    if ext is not None:
+        result["extensions"] = ext
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline()

@@ -51,31 +51,126 @@ __device__ __forceinline__ ChunkBits<F> load_chunk(const uint8_t* __restrict__ p
     return r;
 }
 
-// Decoded value of element j (0..15) of a chunk.  For QSGD `z` is d.
+// Byte k of a word as fp32 (the compiler turns this into v_cvt_f32_ubyte<k>,
+// so the extraction costs nothing).
+__device__ __forceinline__ float byte_f(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+
+// x & mask through v_bitop3 (truth table 0xC0 = a & b).  The builtin is
+// opaque to the optimizer, which would otherwise fold a spread-then-convert
+// back into one bitfield extract per code.
+__device__ __forceinline__ uint32_t and_mask(uint32_t x, uint32_t mask) {
+    return __builtin_amdgcn_bitop3_b32(x, mask, 0u, 0xC0);
+}
+
+// m negated (sign bit flipped) when bit `b` of w is set: one shift and one
+// v_bitop3 (truth table 0x6C = (a & c) ^ b, c = the sign bit).  Equals
+// `bit ? -m : m` for every m.
+__device__ __forceinline__ float neg_if_bit(float m, uint32_t w, int b) {
+    return __uint_as_float(__builtin_amdgcn_bitop3_b32(w << (31 - b), __float_as_uint(m), 0x80000000u, 0x6C));
+}
+
+// a[j] = a[j] + DQ(element j) for the 16 elements of a chunk, each sum
+// rounded once in fp32 exactly as decode-then-add would round it.  Sub-byte
+// codes are first spread one per byte (a few shifts and masks per word), so
+// each code converts with a byte conversion instead of a bitfield extract.
+// For QSGD `z` is d = norm/7.
 template <int F>
-__device__ __forceinline__ float chunk_dq(const ChunkBits<F>& c, int j, float s, float z) {
+__device__ __forceinline__ void add_chunk(float (&a)[16], const ChunkBits<F>& c, float s, float z) {
     const uint32_t words[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
     if constexpr (F == A_U8) {
-        const float p = (float)((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
-        return p + z;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = byte_f(words[j >> 2], j & 3) * s;
+            a[j] = a[j] + (p + z);
+        }
     } else if constexpr (F == A_FP8) {
-        return e4m3_decode((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = a[j] + e4m3_decode((words[j >> 2] >> (8 * (j & 3))) & 0xFFu) * s;
     } else if constexpr (F == A_U4) {
-        const float p = (float)((words[j >> 3] >> (4 * (j & 7))) & 0xFu) * s;
-        return p + z;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // nibbles 0,2,4,6 and 1,3,5,7 of the word, one per byte
+            const uint32_t sp[2] = {and_mask(words[h], 0x0F0F0F0Fu), and_mask(words[h] >> 4, 0x0F0F0F0Fu)};
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const float p = byte_f(sp[n & 1], n >> 1) * s;
+                a[8 * h + n] = a[8 * h + n] + (p + z);
+            }
+        }
     } else if constexpr (F == A_U2) {
-        const float p = (float)((words[0] >> (2 * j)) & 0x3u) * s;
-        return p + z;
+        uint32_t sp[4];  // sp[r] byte q = code 4q + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sp[r] = and_mask(words[0] >> (2 * r), 0x03030303u);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = byte_f(sp[j & 3], j >> 2) * s;
+            a[j] = a[j] + (p + z);
+        }
     } else if constexpr (F == A_TER) {
-        const uint32_t code = (words[0] >> (2 * j)) & 0x3u;
-        return (code & 1u) ? ((code & 2u) ? -s : s) : 0.0f;
+        // The term is 0 or +-s, so fma(f, s, a) with f in {0, 1, -1} is the
+        // exact sum rounded once, as a + DQ is.  f is the 2-bit code read as
+        // a signed field, after clearing bit 1 where bit 0 is clear (the
+        // value of the never-emitted code 2, like code 0, is +0).
+        const uint32_t w = words[0];
+        const uint32_t clean = w & ~((~w & 0x55555555u) << 1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int f = __builtin_amdgcn_sbfe((int)clean, 2 * j, 2);
+            a[j] = __builtin_fmaf((float)f, s, a[j]);
+        }
     } else if constexpr (F == A_QSGD) {
-        const uint32_t code = (words[j >> 3] >> (4 * (j & 7))) & 0xFu;
-        const uint32_t level = code & 7u;
-        const float mag = (float)level * z;
-        return level == 0u ? 0.0f : ((code & 8u) ? -mag : mag);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t sp[2] = {and_mask(words[h], 0x0F0F0F0Fu), and_mask(words[h] >> 4, 0x0F0F0F0Fu)};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t lv = and_mask(sp[e], 0x07070707u);
+                // sign bits (bit 3 of each byte) kept only where the level is
+                // nonzero: level 0 decodes to +0 whatever its sign bit
+                const uint32_t nz = ((lv + 0x7F7F7F7Fu) & 0x80808080u) >> 4;
+                const uint32_t sg = sp[e] & nz;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float mag = byte_f(lv, q) * z;
+                    const int j = 8 * h + 2 * q + e;
+                    a[j] = a[j] + neg_if_bit(mag, sg, 8 * q + 3);
+                }
+            }
+        }
     } else {
-        return ((words[0] >> j) & 1u) ? -s : s;
+        // sign: DQ = bit ? -s : s
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[j] = a[j] + neg_if_bit(s, words[0], j);
+    }
+}
+
+// The fast forms above rely on 0 * s being +0: for TernGrad's s and QSGD's
+// d that holds when the value is +0 or positive and finite.  Otherwise (an
+// overflowed sum of squares gives d = inf; a caller may pass anything) the
+// worker's terms are decoded one by one exactly as the decoder does.
+template <int F>
+__device__ __forceinline__ bool needs_exact_path(float s, float z) {
+    if constexpr (F == A_QSGD) return __float_as_uint(z) >= 0x7F800000u;
+    else if constexpr (F == A_TER) return __float_as_uint(s) >= 0x7F800000u;
+    else return false;
+}
+
+template <int F>
+__device__ __forceinline__ void add_chunk_exact(float (&a)[16], const ChunkBits<F>& c, float s, float z) {
+    const uint32_t w[2] = {c.v.x, c.v.y};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float t;
+        if constexpr (F == A_QSGD) {
+            const uint32_t code = (w[j >> 3] >> (4 * (j & 7))) & 0xFu;
+            const uint32_t level = code & 7u;
+            const float mag = (float)level * z;
+            t = level == 0u ? 0.0f : ((code & 8u) ? -mag : mag);
+        } else {
+            const uint32_t code = (w[0] >> (2 * j)) & 0x3u;
+            t = (code & 1u) ? ((code & 2u) ? -s : s) : 0.0f;
+        }
+        a[j] = a[j] + t;
     }
 }
 
@@ -189,10 +284,15 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                     float s, z;
                     st.get(scale, zero, nb, bk, w0 + u, s, z);
                     if constexpr (F == A_QSGD) z = s / 7.0f;
+                    if (needs_exact_path<F>(s, z)) {
+                        if constexpr (F == A_QSGD || F == A_TER) {
 #pragma unroll
-                    for (int k = 0; k < K; ++k)
+                            for (int k = 0; k < K; ++k) add_chunk_exact<F>(a[k], slot[u][k], s, z);
+                        }
+                    } else {
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) a[k][j] = a[k][j] + chunk_dq<F>(slot[u][k], j, s, z);
+                        for (int k = 0; k < K; ++k) add_chunk<F>(a[k], slot[u][k], s, z);
+                    }
                 }
                 const int32_t w = w0 + UW + u < cend ? w0 + UW + u : cend - 1;
                 load_codes<G, F, FULL>(codes, pbytes, base, n, w, slot[u]);

@@ -309,3 +309,71 @@ def test_random_shapes_low_bit(qc, ora):
         codes, scale, zero = run_uniform(qc, x, None, bucket, 2)
         p, s, z = ora.encode_uniform(x, None, bucket, 2)
         assert bits_equal(codes.host(), p), (trial, n, bucket)
+
+
+# ================================== accumulation of arbitrary payload bits
+
+
+def bits_or_both_nan(got, want):
+    g, w = np.asarray(got, np.float32), np.asarray(want, np.float32)
+    nan = np.isnan(g) & np.isnan(w)
+    return bool(np.all(nan | (g.view(np.uint32) == w.view(np.uint32))))
+
+
+ANY_FMT = {"u8": (0, 8), "u4": (0, 4), "u2": (0, 2), "qsgd": (2, 16), "sign": (3, 1), "ter": (4, 2)}
+ORA_BITS = {"u8": 8, "u4": 4, "u2": 2, "qsgd": 4, "sign": 1, "ter": 2}
+
+
+@pytest.mark.parametrize("fmt", list(ANY_FMT))
+@pytest.mark.parametrize("group", [64, 2048])
+def test_dequant_accumulate_arbitrary_codes_and_scales(qc, ora, fmt, group):
+    """Every code value (including QSGD's level-0 code with its sign bit set
+    and TernGrad's code 2, which the encoders never emit), scales that are
+    negative, -0, +0, tiny or infinite, and a caller's accumulator holding
+    -0: the kernel must add exactly what the decoder's rule gives."""
+    code, bits = ANY_FMT[fmt]
+    m, n = 5, 3 * group + 37
+    nb = qc.nbuckets(n, group)
+    pb = qc.payload_bytes(code, n, group, bits)
+    rng = np.random.default_rng(group + len(fmt))
+    payloads = synth.host_words(m * pb // 4, 31 + group).view(np.uint8).copy()
+    # zero the padding after each payload's last code, as the encoders do
+    valid = ora.payload_bytes(ora.UNIFORM if code == 0 else code, n, ORA_BITS[fmt])
+    used = -(-n * ORA_BITS[fmt] // 8)
+    for w in range(m):
+        payloads[w * pb + used: w * pb + valid] = 0
+    specials = np.array([0.0, -0.0, -1.5, 1e-45, np.inf, 3.0, 1e30], np.float32)
+    scale = rng.normal(0, 1, m * nb).astype(np.float32)
+    scale[: min(specials.size, scale.size)] = specials[: min(specials.size, scale.size)]
+    zero = rng.normal(0, 1, m * nb).astype(np.float32) if code == 0 else None
+    start = synth.host_normal(n, 1.0, seed=5)
+    start[::3] = -0.0
+    want = ora.dequant_accumulate(code, payloads, scale, zero, m, n, group, ORA_BITS[fmt], acc=start)
+    acc = out_f32(n)
+    acc.t.copy_(dev(start))
+    qc.qc_dequant_accumulate(code, dev(payloads), dev(scale), None if zero is None else dev(zero), m, n,
+                             group, bits, acc.t, True)
+    sync()
+    assert bits_or_both_nan(acc.f32(), want), first_diff(acc.f32(), want)
+
+
+def test_qsgd_accumulate_with_overflowing_norm(qc, ora):
+    """Huge but finite gradients: a bucket's sum of squares overflows, the
+    norm is +inf, every level is 0, and the sum must stay exact (+0 terms)."""
+    B, n, m = 512, 4 * 512, 3
+    parts, norms = [], []
+    for w in range(m):
+        x = synth.host_laplace(n, 1e-3, seed=900 + w)
+        x[B: 2 * B] = np.float32(3e19) * np.sign(x[B: 2 * B])   # this bucket's norm overflows
+        p, nr = ora.encode_qsgd(x, None, B, 17 + w)
+        parts.append(p)
+        norms.append(nr)
+    assert np.isinf(norms[0][1])
+    payloads, norm = np.concatenate(parts), np.concatenate(norms)
+    start = np.full(n, -0.0, np.float32)
+    want = ora.dequant_accumulate(2, payloads, norm, None, m, n, B, 4, acc=start)
+    acc = out_f32(n)
+    acc.t.copy_(dev(start))
+    qc.qc_dequant_accumulate(2, dev(payloads), dev(norm), None, m, n, B, 16, acc.t, True)
+    sync()
+    assert bits_or_both_nan(acc.f32(), want), first_diff(acc.f32(), want)
