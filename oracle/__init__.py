@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qc_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-UNIFORM, FP8_ROWWISE, QSGD, SIGN, TERNARY = 0, 1, 2, 3, 4
+UNIFORM, FP8_ROWWISE, QSGD, SIGN, TERNARY, INT8_SHARED = 0, 1, 2, 3, 4, 5
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -74,6 +74,11 @@ def lib():
         L.qco_decode_one.restype = ctypes.c_float
         L.qco_dequant_accumulate.argtypes = [I32, P, P, P, I32, I64, I32, I32, P, I32]
         L.qco_majority_vote.argtypes = [P, I32, I64, P]
+        L.qco_bucket_absmax.argtypes = [P, P, I64, I32, P]
+        L.qco_absmax_combine.argtypes = [P, I32, I64, P]
+        L.qco_encode_int8_shared.argtypes = [P, P, I64, I32, P, P, P]
+        L.qco_decode_int8_shared.argtypes = [P, P, I64, I32, P]
+        L.qco_sum_int8_shared.argtypes = [P, I32, I64, I32, P, P, I32, P]
         _lib = L
     return _lib
 
@@ -260,3 +265,49 @@ def majority_vote(payloads, m: int, n: int):
     out = np.empty(payload_bytes(SIGN, n, 1), dtype=np.uint8)
     lib().qco_majority_vote(_p(payloads), m, n, _p(out))
     return out
+
+
+# ------------------------------------------------------ shared-scale INT8
+
+
+def bucket_absmax(x, ef, bucket: int):
+    x = _f32(x)
+    amax = np.empty(nbuckets(x.size, bucket), dtype=np.float32)
+    lib().qco_bucket_absmax(_p(x), _p(None if ef is None else _f32(ef)), x.size, bucket, _p(amax))
+    return amax
+
+
+def absmax_combine(amax, m: int, nb: int):
+    amax = _f32(amax)
+    out = np.empty(nb, dtype=np.float32)
+    lib().qco_absmax_combine(_p(amax), m, nb, _p(out))
+    return out
+
+
+def encode_int8_shared(x, ef, bucket: int, amax):
+    """Returns (payload uint8, scale float32); ef (if given) is updated."""
+    x = _f32(x)
+    ef = _ef(ef)
+    n = x.size
+    payload = np.empty(payload_bytes(INT8_SHARED, n, 8), dtype=np.uint8)
+    scale = np.empty(nbuckets(n, bucket), dtype=np.float32)
+    lib().qco_encode_int8_shared(_p(x), _p(ef), n, bucket, _p(_f32(amax)), _p(payload), _p(scale))
+    return payload, scale
+
+
+def decode_int8_shared(payload, scale, n: int, bucket: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_int8_shared(_p(np.ascontiguousarray(payload, np.uint8)), _p(_f32(scale)), n, bucket,
+                                 _p(out))
+    return out
+
+
+def sum_int8_shared(payloads, m: int, n: int, bucket: int, scale, isum=None):
+    """Returns (isum int32, out float32).  If ``isum`` is given it is the
+    running integer sum to continue from (it is not modified)."""
+    payloads = np.ascontiguousarray(payloads, np.uint8)
+    acc = np.zeros(n, dtype=np.int32) if isum is None else np.array(isum, dtype=np.int32, copy=True)
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_sum_int8_shared(_p(payloads), m, n, bucket, _p(_f32(scale)), _p(acc), 0 if isum is None else 1,
+                              _p(out))
+    return acc, out

@@ -551,6 +551,96 @@ void qco_decode_sign(const uint8_t* payload, const float* scale, int64_t n,
 /* receive side                                                          */
 /* ------------------------------------------------------------------ */
 
+/* ------------------------------------------------------------------ */
+/* shared-scale INT8  [QCD, "Quantization-Aware All-Reduce": local and  */
+/*   distributed quantization; QCD, "Practical Considerations":         */
+/*   synchronization of scale and zero point; GCQC, "Why sparsification */
+/*   fights the all-reduce": compressed forms that can be summed]       */
+/* ------------------------------------------------------------------ */
+/* Readings: the ranks agree one scale per bucket before they encode: the
+ * largest |v| that any rank holds in the bucket (each rank's local maximum,
+ * combined with max, as an all-reduce would).  Codes are symmetric signed
+ * INT8 in [-127, 127] with no zero point, so a sum of codes is an exact
+ * integer and the receiver dequantizes it once (quantize locally, reduce the
+ * quantized data, dequantize after the reduction).  scale = amax/127;
+ * code = rint(v/scale) clamped to [-127, 127]; scale 0 gives code 0;
+ * DQ = code * scale; ef = v - DQ. */
+
+void qco_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    for (int64_t k = 0; k < nb; ++k) {
+        const int64_t lo = k * bucket;
+        const int64_t hi = (lo + bucket <= n) ? lo + bucket : n;
+        float m = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            const float v = ef ? ef[i] + x[i] : x[i];
+            if (fabsf(v) > m)
+                m = fabsf(v);
+        }
+        amax[k] = m;
+    }
+}
+
+void qco_absmax_combine(const float* amax, int32_t m, int64_t nb, float* out)
+{
+    for (int64_t k = 0; k < nb; ++k) {
+        float r = amax[k];
+        for (int32_t w = 1; w < m; ++w)
+            if (amax[(int64_t)w * nb + k] > r)
+                r = amax[(int64_t)w * nb + k];
+        out[k] = r;
+    }
+}
+
+void qco_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket,
+                            const float* amax, uint8_t* payload, float* scale)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    memset(payload, 0, (size_t)qco_payload_bytes(QCO_INT8_SHARED, n, 8));
+    for (int64_t k = 0; k < nb; ++k) {
+        const float sc = amax[k] / 127.0f;
+        const int64_t lo = k * bucket;
+        const int64_t hi = (lo + bucket <= n) ? lo + bucket : n;
+        for (int64_t i = lo; i < hi; ++i) {
+            const float v = ef ? ef[i] + x[i] : x[i];
+            int32_t q = 0;
+            if (sc != 0.0f) {
+                float r = rintf(v / sc);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q = (int32_t)r;
+            }
+            payload[i] = (uint8_t)(int8_t)q;
+            if (ef)
+                ef[i] = v - (float)q * sc;
+        }
+        scale[k] = sc;
+    }
+}
+
+void qco_decode_int8_shared(const uint8_t* payload, const float* scale, int64_t n,
+                            int32_t bucket, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)(int8_t)payload[i] * scale[i / bucket];
+}
+
+void qco_sum_int8_shared(const uint8_t* payloads, int32_t m, int64_t n, int32_t bucket,
+                         const float* scale, int32_t* isum, int32_t accumulate, float* out)
+{
+    const int64_t pb = qco_payload_bytes(QCO_INT8_SHARED, n, 8);
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = (accumulate && isum) ? isum[i] : 0;
+        for (int32_t w = 0; w < m; ++w)
+            t += (int8_t)payloads[(int64_t)w * pb + i];
+        if (isum)
+            isum[i] = (int32_t)t;
+        if (out)
+            out[i] = (float)(int32_t)t * scale[i / bucket];
+    }
+}
+
 float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,
                      const float* zero, int64_t i, int32_t group, int32_t bits)
 {
@@ -564,6 +654,8 @@ float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,
         return qsgd_dq(get_nibble(payload, i), scale[k] / 7.0f);
     case QCO_TERNARY:
         return ternary_dq(get_crumb(payload, i), scale[k]);
+    case QCO_INT8_SHARED:
+        return (float)(int8_t)payload[i] * scale[k];
     default: /* QCO_SIGN */
         return get_bit(payload, i) ? -scale[k] : scale[k];
     }

@@ -38,7 +38,8 @@
 extern "C" {
 #endif
 
-enum { QCO_UNIFORM = 0, QCO_FP8_ROWWISE = 1, QCO_QSGD = 2, QCO_SIGN = 3, QCO_TERNARY = 4 };
+enum { QCO_UNIFORM = 0, QCO_FP8_ROWWISE = 1, QCO_QSGD = 2, QCO_SIGN = 3, QCO_TERNARY = 4,
+       QCO_INT8_SHARED = 5 };
 
 /* Bytes of one payload of n elements (see conventions above). */
 int64_t qco_payload_bytes(int32_t fmt, int64_t n, int32_t bits);
@@ -95,6 +96,25 @@ void qco_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket,
                         uint8_t* payload, float* scale);
 void qco_decode_ternary(const uint8_t* payload, const float* scale, int64_t n,
                         int32_t bucket, float* out);
+
+/* Shared-scale INT8 ("distributed quantization"): every worker encodes a
+ * bucket with the same scale, derived from the largest |v| any worker holds
+ * there, so the workers' codes add exactly as integers.
+ *   qco_bucket_absmax:   amax[k] = max |x + ef| over bucket k (ef may be NULL).
+ *   qco_absmax_combine:  out[k] = max over m arrays amax[w*nb + k].
+ *   qco_encode_int8_shared: scale = amax/127, symmetric codes in [-127, 127]
+ *                        (one int8 per element), error feedback (ef may be NULL).
+ *   qco_sum_int8_shared: isum[i] = (accumulate ? isum[i] : 0) + sum of the m
+ *                        workers' codes (exact); out[i] = (float)isum[i] * scale.
+ *                        isum or out may be NULL (not both); accumulate needs isum. */
+void qco_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax);
+void qco_absmax_combine(const float* amax, int32_t m, int64_t nb, float* out);
+void qco_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket,
+                            const float* amax, uint8_t* payload, float* scale);
+void qco_decode_int8_shared(const uint8_t* payload, const float* scale, int64_t n,
+                            int32_t bucket, float* out);
+void qco_sum_int8_shared(const uint8_t* payloads, int32_t m, int64_t n, int32_t bucket,
+                         const float* scale, int32_t* isum, int32_t accumulate, float* out);
 
 /* Element i of a payload decoded to fp32, for any format. */
 float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,

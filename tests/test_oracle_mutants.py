@@ -23,6 +23,7 @@ def _load(name, path):
 PIN_MODULES = [
     _load("oracle_pins_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins.py")),
     _load("oracle_pins_stochastic_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_stochastic.py")),
+    _load("oracle_pins_shared_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_shared.py")),
 ]
 
 
@@ -95,6 +96,24 @@ MUTANTS = [
      ["test_accumulate_vs_exact_sum"]),
     ("acc_drops_last_worker", "for (int32_t w = 0; w < m; ++w) {\n            float dq",
      "for (int32_t w = 0; w < m - 1; ++w) {\n            float dq", ["test_accumulate_vs_exact_sum"]),
+    ("shared_scale_128", "const float sc = amax[k] / 127.0f;", "const float sc = amax[k] / 128.0f;",
+     ["test_int8_shared_on_grid_is_exact", "test_int8_shared_brute_force_nearest"]),
+    ("shared_rounds_down", "float r = rintf(v / sc);", "float r = floorf(v / sc);",
+     ["test_int8_shared_brute_force_nearest", "test_int8_shared_symmetric"]),
+    ("shared_clamps_at_128", "if (r < -127.0f) r = -127.0f;", "if (r < -128.0f) r = -128.0f;",
+     ["test_int8_shared_saturates_and_zero_scale"]),
+    ("shared_absmax_ignores_ef", "const float v = ef ? ef[i] + x[i] : x[i];\n            if (fabsf(v) > m)",
+     "const float v = x[i];\n            if (fabsf(v) > m)", ["test_bucket_absmax_matches_numpy"]),
+    ("shared_combine_takes_min", "if (amax[(int64_t)w * nb + k] > r)", "if (amax[(int64_t)w * nb + k] < r)",
+     ["test_absmax_combine_is_elementwise_max", "test_every_worker_agrees_on_the_scale"]),
+    ("shared_sum_skips_first_worker", "for (int32_t w = 0; w < m; ++w)\n            t +=",
+     "for (int32_t w = 1; w < m; ++w)\n            t +=", ["test_sum_int8_shared_is_the_exact_integer_sum"]),
+    ("shared_sum_ignores_running_sum", "int64_t t = (accumulate && isum) ? isum[i] : 0;", "int64_t t = 0;",
+     ["test_sum_int8_shared_is_the_exact_integer_sum"]),
+    ("shared_decode_unsigned", "out[i] = (float)(int8_t)payload[i] * scale[i / bucket];",
+     "out[i] = (float)payload[i] * scale[i / bucket];", ["test_int8_shared_on_grid_is_exact"]),
+    ("shared_ef_not_updated", "ef[i] = v - (float)q * sc;", "ef[i] = v;",
+     ["test_int8_shared_on_grid_is_exact", "test_int8_shared_error_bound_and_feedback"]),
 ]
 
 
@@ -127,6 +146,8 @@ def _run_pin(fn, mod, rocrand_philox):
         variants = [{"bits": 8}, {"bits": 4}, {"bits": 2}]
     if "fmt" in sig.parameters:
         variants = [{"fmt": f} for f in ("fp8", "qsgd", "sign", "int4")]
+    if "with_ef" in sig.parameters:
+        variants = [{"with_ef": False}, {"with_ef": True}]
     for v in variants:
         fn(**kw, **v)
 
