@@ -14,9 +14,11 @@ synthetic input, every op at its full workload size:
 Beside the step, in a timed region of its own that `value` does not
 include, the low-bit extensions run on the same 1e9-element gradient:
 2-bit uniform and 4-bit stochastic uniform (buckets of 512, error
-feedback), TernGrad (buckets of 512, error feedback), their decoders, and
-the receive-side sum of 64 workers' TernGrad and 2-bit payloads of 2^26
-(the 2-bit sum requantized to 2 bits in the same pass).  They are reported
+feedback), TernGrad (buckets of 512, error feedback), shared-scale INT8
+(the per-bucket max statistic and the encode with an agreed maximum, error
+feedback), their decoders, and the receive-side sums of 64 workers'
+payloads of 2^26: TernGrad, 2-bit (requantized to 2 bits in the same
+pass) and shared-scale INT8 (an exact integer sum, dequantized once).  They are reported
 under `extensions`, in the same form as `ops`.
 
 Encoders run first and decoders later in the step, so a decoder never
@@ -103,12 +105,18 @@ def ext_bytes():
         "tern_dec": (4 * X_N, X_N // 4 + 4 * nbx + 4 * X_N),
         "acc_tern": (4 * X_M * X_AN, X_M * (X_AN // 4 + 4 * nba) + 4 * X_AN),
         "acc_int2_requant": (4 * X_M * X_AN, X_M * (X_AN // 4 + 8 * nba) + 4 * X_AN + X_AN // 4 + 8 * nba),
+        # shared-scale INT8: the local statistic (x + ef read), the encode
+        # with the agreed maximum, and the exact integer sum of 64 workers
+        "shared_absmax": (4 * X_N, 8 * X_N + 4 * nbx),
+        "shared_enc": (4 * X_N, 12 * X_N + X_N + 8 * nbx),
+        "shared_sum": (4 * X_M * X_AN, X_M * X_AN + 4 * X_AN + 4 * nba),
     }
 
 
 ORDER = ["uniform_enc", "qsgd_enc", "fp8_enc", "sign_enc", "acc_requant", "sign_vote", "qsgd_dec",
          "fp8_dec", "sign_dec", "uniform_dec"]
-EXT_ORDER = ["int2_enc", "stoch4_enc", "tern_enc", "acc_tern", "acc_int2_requant", "int2_dec", "tern_dec"]
+EXT_ORDER = ["int2_enc", "stoch4_enc", "tern_enc", "shared_absmax", "shared_enc", "acc_tern", "acc_int2_requant",
+             "shared_sum", "int2_dec", "tern_dec"]
 
 
 # ------------------------------------------------------------- GPU setup
@@ -195,6 +203,27 @@ def setup_ext(qc, synth, torch, st, empty):
         qc.qc_encode_uniform(g, None, X_AN, X_AB, 2, st["xa_i2"][w * pbi:(w + 1) * pbi], st["xa_i2s"][sl],
                              st["xa_i2z"][sl])
         del g
+    # shared-scale INT8: every worker's bucket maxima, combined, then each
+    # worker encodes with the agreed scale (its gradient drawn again)
+    st["x_amax"] = torch.empty(nbx, dtype=F32, device=dev)
+    st["x_i8s"] = empty(qc.payload_bytes(qc.QC_INT8_SHARED, X_N, X_B, 8))
+    st["x_i8ss"] = torch.empty(nbx, dtype=F32, device=dev)
+    qc.qc_bucket_absmax(st["c3_x"], None, X_N, X_B, st["x_amax"])
+    pbs = qc.payload_bytes(qc.QC_INT8_SHARED, X_AN, X_AB, 8)
+    stats = torch.empty(X_M * nba, dtype=F32, device=dev)
+    for w in range(X_M):
+        g = synth.device_outlier_grad(X_AN, 1e-3, 0.01, 100.0, 6000 + w, dev)
+        qc.qc_bucket_absmax(g, None, X_AN, X_AB, stats[w * nba:(w + 1) * nba])
+        del g
+    st["xs_amax"] = torch.empty(nba, dtype=F32, device=dev)
+    qc.qc_absmax_combine(stats, X_M, nba, st["xs_amax"])
+    st["xs_codes"] = empty(X_M * pbs)
+    st["xs_scale"] = torch.empty(nba, dtype=F32, device=dev)
+    for w in range(X_M):
+        g = synth.device_outlier_grad(X_AN, 1e-3, 0.01, 100.0, 6000 + w, dev)
+        qc.qc_encode_int8_shared(g, None, X_AN, X_AB, st["xs_amax"], st["xs_codes"][w * pbs:(w + 1) * pbs],
+                                 st["xs_scale"])
+        del g
     st["xa_acc"] = torch.empty(X_AN, dtype=F32, device=dev)
     st["xa_rq"] = empty(pbi)
     st["xa_rqs"] = torch.empty(nba, dtype=F32, device=dev)
@@ -233,6 +262,11 @@ def make_ops(qc, st):
         "int2_dec": lambda: qc.qc_decode(qc.QC_UNIFORM, s["x_i2"], s["x_i2s"], s["x_i2z"], X_N, X_B, 2,
                                          s["c3_out"]),
         "tern_dec": lambda: qc.qc_decode(qc.QC_TERNARY, s["x_t"], s["x_ts"], None, X_N, X_B, 2, s["c3_out"]),
+        "shared_absmax": lambda: qc.qc_bucket_absmax(s["c3_x"], s["x_ef"], X_N, X_B, s["x_amax"]),
+        "shared_enc": lambda: qc.qc_encode_int8_shared(s["c3_x"], s["x_ef"], X_N, X_B, s["x_amax"], s["x_i8s"],
+                                                       s["x_i8ss"]),
+        "shared_sum": lambda: qc.qc_sum_int8_shared(s["xs_codes"], X_M, X_AN, X_AB, s["xs_scale"], None, False,
+                                                    s["xa_acc"]),
         "acc_tern": lambda: qc.qc_dequant_accumulate(qc.QC_TERNARY, s["xa_t"], s["xa_ts"], None, X_M, X_AN,
                                                      X_AB, 2, s["xa_acc"], False),
         "acc_int2_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["xa_i2"], s["xa_i2s"], s["xa_i2z"],
@@ -483,8 +517,9 @@ def main():
             "qsgd": f"{C3_N} fp32, bucket {C3_B}, s=16, EF",
             "sign": f"{C4_N} bf16, bucket {C4_B}, EF; vote M={C4_M}",
             "accumulate": f"M={C5_M} x {C5_N} INT8, bucket {C5_B}, fused INT8 requant",
-            "extensions": (f"outside the step: {X_N} fp32, bucket {X_B}, EF: INT2, stochastic INT4, TernGrad "
-                           f"+ decode; M={X_M} x {X_AN}, bucket {X_AB}: TernGrad sum, INT2 sum + INT2 requant"),
+            "extensions": (f"outside the step: {X_N} fp32, bucket {X_B}, EF: INT2, stochastic INT4, TernGrad, "
+                           f"shared-scale INT8 (max statistic + encode) + decode; M={X_M} x {X_AN}, bucket "
+                           f"{X_AB}: TernGrad sum, INT2 sum + INT2 requant, shared-scale INT8 integer sum"),
         },
         "hbm_frac_step": round(sum(sizes[o][1] for o in names) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     QC_ERR_UNSUPPORTED,
     QC_F32,
     QC_FP8_ROWWISE,
+    QC_INT8_SHARED,
     QC_MAX_BUCKET,
     QC_MAX_WORKERS,
     QC_MIN_BUCKET,
@@ -28,9 +29,12 @@ from .binding import (  # noqa: F401
     lib,
     nbuckets,
     payload_bytes,
+    qc_absmax_combine,
+    qc_bucket_absmax,
     qc_decode,
     qc_dequant_accumulate,
     qc_encode_fp8_rowwise,
+    qc_encode_int8_shared,
     qc_encode_qsgd,
     qc_encode_sign,
     qc_encode_ternary,
@@ -39,4 +43,5 @@ from .binding import (  # noqa: F401
     qc_majority_vote,
     qc_payload_bytes,
     qc_status_str,
+    qc_sum_int8_shared,
 )

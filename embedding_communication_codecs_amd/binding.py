@@ -18,13 +18,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqc.so")
 
 QC_OK, QC_ERR_ARG, QC_ERR_ALIGN, QC_ERR_UNSUPPORTED, QC_ERR_LAUNCH = 0, 1, 2, 3, 4
-QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN, QC_TERNARY = 0, 1, 2, 3, 4
+QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN, QC_TERNARY, QC_INT8_SHARED = 0, 1, 2, 3, 4, 5
 QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
 
 EXPORTS = (
     "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_fp8_rowwise", "qc_encode_qsgd",
-    "qc_encode_ternary", "qc_encode_sign", "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
+    "qc_encode_ternary", "qc_encode_sign", "qc_bucket_absmax", "qc_absmax_combine", "qc_encode_int8_shared",
+    "qc_sum_int8_shared", "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
 
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
             "qc_decode": [I32, P, P, P, I64, I32, I32, P, P],
             "qc_dequant_accumulate": [I32, P, P, P, I32, I64, I32, I32, P, I32, P, P, P, P],
             "qc_majority_vote": [P, I32, I64, P, P],
+            "qc_bucket_absmax": [P, P, I64, I32, P, P],
+            "qc_absmax_combine": [P, I32, I64, P, P],
+            "qc_encode_int8_shared": [P, P, I64, I32, P, P, P, P],
+            "qc_sum_int8_shared": [P, I32, I64, I32, P, P, I32, P, P],
             "qc_payload_bytes": [I32, I64, I32, I32],
             "qc_status_str": [I32],
         }
@@ -190,6 +195,34 @@ def qc_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, acc, accum
         _ptr(zero, 4 * mm * nb, "zero"), m, n, group, bits, _ptr(acc, 4 * n, "acc"),
         1 if accumulate else 0, _ptr(rq_codes, rq_pb, "rq_codes"), _ptr(rq_scale, 4 * nb, "rq_scale"),
         _ptr(rq_zero, 4 * nb, "rq_zero"), _stream(stream)))
+
+
+def qc_bucket_absmax(x, ef, n, bucket, amax, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    _check(lib().qc_bucket_absmax(_ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket,
+                                  _ptr(amax, 4 * nb, "amax"), _stream(stream)))
+
+
+def qc_absmax_combine(amax, m, nb, out, stream=None):
+    _check(lib().qc_absmax_combine(_ptr(amax, 4 * max(m, 0) * max(nb, 0), "amax"), m, nb,
+                                   _ptr(out, 4 * max(nb, 0), "out"), _stream(stream)))
+
+
+def qc_encode_int8_shared(x, ef, n, bucket, amax, codes, scale, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_INT8_SHARED, n, bucket, 8) if n >= 0 else None
+    _check(lib().qc_encode_int8_shared(
+        _ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, _ptr(amax, 4 * nb, "amax"),
+        _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"), _stream(stream)))
+
+
+def qc_sum_int8_shared(codes, m, n, bucket, scale, isum, accumulate, out, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_INT8_SHARED, n, bucket, 8) if n >= 0 else None
+    _check(lib().qc_sum_int8_shared(
+        _ptr(codes, max(m, 0) * pb if pb is not None else None, "codes"), m, n, bucket,
+        _ptr(scale, 4 * nb, "scale"), _ptr(isum, 4 * max(n, 0), "isum"), 1 if accumulate else 0,
+        _ptr(out, 4 * max(n, 0), "out"), _stream(stream)))
 
 
 def qc_majority_vote(words, m, n, out_words, stream=None):

@@ -33,7 +33,8 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
 ]
-SOURCES = ["k_encode.hip", "k_fp8.hip", "k_decode.hip", "k_accumulate.hip", "k_vote.hip", "qc_api.cpp"]
+SOURCES = ["k_encode.hip", "k_fp8.hip", "k_decode.hip", "k_accumulate.hip", "k_vote.hip", "k_shared_sum.hip",
+           "qc_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -16,13 +16,13 @@
 namespace qc {
 namespace {
 
-enum { F_U8 = 0, F_U4 = 1, F_FP8 = 2, F_QSGD = 3, F_SIGN = 4, F_U2 = 5, F_TER = 6 };
+enum { F_U8 = 0, F_U4 = 1, F_FP8 = 2, F_QSGD = 3, F_SIGN = 4, F_U2 = 5, F_TER = 6, F_I8S = 7 };
 
 // The code bits of chunk c (elements 4c..4c+3) in the low bits.
 template <int F>
 __device__ __forceinline__ uint32_t chunk_word(const uint8_t* __restrict__ codes, int64_t c) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(codes);
-    if constexpr (F == F_U8 || F == F_FP8) return w[c];
+    if constexpr (F == F_U8 || F == F_FP8 || F == F_I8S) return w[c];
     else if constexpr (F == F_U4 || F == F_QSGD) return w[c >> 1] >> ((c & 1) * 16);
     else if constexpr (F == F_U2 || F == F_TER) return w[c >> 2] >> ((c & 3) * 8);
     else return w[c >> 3] >> ((c & 7) * 4);
@@ -45,6 +45,8 @@ __device__ __forceinline__ float chunk_value(uint32_t w, int j, float s, float z
         return (code & 1u) ? ((code & 2u) ? -s : s) : 0.0f;
     } else if constexpr (F == F_FP8) {
         return e4m3_decode((w >> (8 * j)) & 0xFFu) * s;
+    } else if constexpr (F == F_I8S) {
+        return (float)(int32_t)(int8_t)(w >> (8 * j)) * s;
     } else if constexpr (F == F_QSGD) {
         const uint32_t code = (w >> (4 * j)) & 0xFu;
         const uint32_t level = code & 7u;
@@ -131,6 +133,8 @@ hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, con
             return launch<F_U2, true>(codes, scale, zero, n, group, out, stream);
         case 4:  // ternary
             return launch<F_TER, true>(codes, scale, zero, n, group, out, stream);
+        case 5:  // shared-scale int8
+            return launch<F_I8S, true>(codes, scale, zero, n, group, out, stream);
         case 1:  // rowwise fp8: group = dim, any multiple of 4
             if ((group & (group - 1)) == 0)
                 return launch<F_FP8, true>(codes, scale, zero, n, group, out, stream);

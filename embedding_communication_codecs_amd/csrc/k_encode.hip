@@ -430,6 +430,85 @@ k_enc_sign(const void* __restrict__ x, float* __restrict__ ef, int64_t n, int64_
     }
 }
 
+// ===================================================== shared-scale INT8
+// The bucket statistic each worker contributes: amax = max |v|.  After the
+// workers' maxima are combined (max over workers), every worker encodes
+// with scale = amax/127: code = rint(v/scale) clamped to [-127, 127] as an
+// int8 byte (0 when scale is 0); DQ = code*scale; ef = v - DQ.
+
+template <class G, bool EF, bool FULL>
+__device__ __forceinline__ void absmax_bucket(const float* __restrict__ x, const float* __restrict__ ef,
+                                              int64_t n, int64_t bk, float* __restrict__ amax, float* lds) {
+    constexpr int K = G::K, LPB = G::LPB;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+    float v[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+    float m = 0.0f;  // masked elements load as 0 and do not change the max
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(v[k][j]));
+    m = group_max<LPB>(m);
+    if constexpr (G::W > 1) m = block_max<G::W>(m, lds);
+    if (bucket_leader<G>()) amax[bk] = m;
+}
+
+template <class G, bool EF>
+__global__ void __launch_bounds__(G::THREADS)
+k_bucket_absmax(const float* __restrict__ x, const float* __restrict__ ef, int64_t n, int64_t nb,
+                float* __restrict__ amax) {
+    __shared__ float lds[G::W];
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        if ((bk + 1) * (int64_t)G::B <= n)
+            absmax_bucket<G, EF, true>(x, ef, n, bk, amax, lds);
+        else
+            absmax_bucket<G, EF, false>(x, ef, n, bk, amax, lds);
+    }
+}
+
+template <class G, bool EF, bool FULL>
+__device__ __forceinline__ void int8s_bucket(const float* __restrict__ x, float* __restrict__ ef, int64_t n,
+                                             int64_t bk, const float* __restrict__ amax,
+                                             uint8_t* __restrict__ codes, int64_t pbytes,
+                                             float* __restrict__ scale) {
+    constexpr int K = G::K, LPB = G::LPB;
+    const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+    float v[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+    const float sc = amax[bk] / 127.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = base + (int64_t)k * LPB * 4;
+        uint32_t q[4];
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int32_t c = 0;
+            if (sc != 0.0f) c = (int32_t)fminf(fmaxf(__builtin_rintf(v[k][j] / sc), -127.0f), 127.0f);
+            q[j] = (uint32_t)c & 0xFFu;  // masked elements are 0 and give code 0
+            e[j] = v[k][j] - (float)c * sc;
+        }
+        store_codes4<8>(codes, i, pbytes, q);
+        if constexpr (EF) store_ef4<FULL>(ef, i, n, e);
+    }
+    if (bucket_leader<G>()) scale[bk] = sc;
+}
+
+template <class G, bool EF>
+__global__ void __launch_bounds__(G::THREADS)
+k_enc_int8_shared(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb,
+                  const float* __restrict__ amax, uint8_t* __restrict__ codes, int64_t pbytes,
+                  float* __restrict__ scale) {
+    for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
+        if ((bk + 1) * (int64_t)G::B <= n)
+            int8s_bucket<G, EF, true>(x, ef, n, bk, amax, codes, pbytes, scale);
+        else
+            int8s_bucket<G, EF, false>(x, ef, n, bk, amax, codes, pbytes, scale);
+    }
+}
+
 // ============================================================ dispatch
 // Geometry per bucket size: LPB lanes per bucket, K chunks per lane, W waves
 // per bucket.  A single wave holds up to K = 8 chunks per lane (32 or 64
@@ -542,6 +621,35 @@ hipError_t launch_encode_sign(const void* x, bool bf16, float* ef, int64_t n, in
     };
     if (bf16) return dispatch_bucket<8>(bucket, [&](auto g) { return body(g, std::true_type{}); });
     return dispatch_bucket<4>(bucket, [&](auto g) { return body(g, std::false_type{}); });
+}
+
+hipError_t launch_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax,
+                                hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            hipLaunchKernelGGL((k_bucket_absmax<G, EF>), grid, block, 0, stream, x, ef, n, nb, amax);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t launch_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket, const float* amax,
+                                     uint8_t* codes, int64_t payload_bytes, float* scale, hipStream_t stream) {
+    const int64_t nb = (n + bucket - 1) / bucket;
+    return dispatch_bucket<4>(bucket, [&](auto g) {
+        using G = decltype(g);
+        const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
+        return with_flag(ef != nullptr, [&](auto has_ef) {
+            constexpr bool EF = decltype(has_ef)::value;
+            hipLaunchKernelGGL((k_enc_int8_shared<G, EF>), grid, block, 0, stream, x, ef, n, nb, amax, codes,
+                               payload_bytes, scale);
+            return hipGetLastError();
+        });
+    });
 }
 
 }  // namespace qc

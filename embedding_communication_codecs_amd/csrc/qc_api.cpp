@@ -48,6 +48,7 @@ int64_t qc_payload_bytes(int32_t fmt, int64_t n, int32_t group, int32_t bits) {
         case QC_QSGD: code_bytes = 4 * ceil_div(n, 8); break;
         case QC_SIGN: code_bytes = 4 * ceil_div(n, 32); break;
         case QC_TERNARY: code_bytes = 4 * ceil_div(n, 16); break;
+        case QC_INT8_SHARED: code_bytes = n; break;
         default: return -1;
     }
     return ceil_div(code_bytes, 16) * 16;
@@ -173,6 +174,10 @@ int check_format(int32_t fmt, int64_t n, int32_t group, int32_t bits, const floa
         case QC_TERNARY:
             if (bits != 2) return QC_ERR_UNSUPPORTED;
             return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
+        case QC_INT8_SHARED:
+            // payloads with one shared scale are summed by qc_sum_int8_shared
+            if (bits != 8 || accumulate_path) return QC_ERR_UNSUPPORTED;
+            return bad_bucket(group) ? QC_ERR_ARG : QC_OK;
         default:
             return QC_ERR_UNSUPPORTED;
     }
@@ -213,6 +218,50 @@ int qc_dequant_accumulate(int32_t fmt, const void* codes, const float* scale, co
     return launched(qc::launch_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, pbytes,
                                                   acc, accumulate != 0, rq_codes, rq_scale, rq_zero,
                                                   hs(stream)));
+}
+
+int qc_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax,
+                     qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!x || !amax) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(amax)) return QC_ERR_ALIGN;
+    return launched(qc::launch_bucket_absmax(x, ef, n, bucket, amax, hs(stream)));
+}
+
+int qc_absmax_combine(const float* amax, int32_t m, int64_t nb, float* out, qc_stream_t stream) {
+    if (nb < 0 || m < 1 || m > QC_MAX_WORKERS || nb > kMaxBuckets) return QC_ERR_ARG;
+    if (nb == 0) return QC_OK;
+    if (!amax || !out) return QC_ERR_ARG;
+    if (misaligned(amax) || misaligned(out)) return QC_ERR_ALIGN;
+    return launched(qc::launch_absmax_combine(amax, m, nb, out, hs(stream)));
+}
+
+int qc_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket, const float* amax,
+                          uint8_t* codes, float* scale, qc_stream_t stream) {
+    if (n < 0 || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!x || !amax || !codes || !scale) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned(amax) || misaligned(codes) || misaligned(scale))
+        return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_int8_shared(x, ef, n, bucket, amax, codes,
+                                                  qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8), scale,
+                                                  hs(stream)));
+}
+
+int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucket, const float* scale,
+                       int32_t* isum, int32_t accumulate, float* out, qc_stream_t stream) {
+    if (n < 0 || m < 1 || m > QC_MAX_WORKERS || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (!isum && !out) return QC_ERR_ARG;
+    if (accumulate && !isum) return QC_ERR_ARG;
+    if (n == 0) return QC_OK;
+    if (!codes || (out && !scale)) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(codes) || misaligned(scale) || misaligned(isum) || misaligned(out)) return QC_ERR_ALIGN;
+    return launched(qc::launch_sum_int8_shared(codes, m, n, bucket, qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8),
+                                               scale, isum, accumulate != 0, out, hs(stream)));
 }
 
 int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_words,

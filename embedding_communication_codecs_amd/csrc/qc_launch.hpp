@@ -46,6 +46,18 @@ hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float
                                      bool accumulate, void* rq_codes, float* rq_scale,
                                      float* rq_zero, hipStream_t stream);
 
+hipError_t launch_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax,
+                                hipStream_t stream);
+
+hipError_t launch_absmax_combine(const float* amax, int32_t m, int64_t nb, float* out, hipStream_t stream);
+
+hipError_t launch_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket, const float* amax,
+                                     uint8_t* codes, int64_t payload_bytes, float* scale, hipStream_t stream);
+
+hipError_t launch_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucket,
+                                  int64_t payload_bytes, const float* scale, int32_t* isum, bool accumulate,
+                                  float* out, hipStream_t stream);
+
 hipError_t launch_majority_vote(const uint32_t* words, int32_t m, int64_t n, int64_t payload_bytes,
                                 uint32_t* out_words, hipStream_t stream);
 

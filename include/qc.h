@@ -59,7 +59,14 @@ enum qc_status {
     QC_ERR_LAUNCH = 4        /* the HIP runtime refused the kernel launch */
 };
 
-enum qc_format { QC_UNIFORM = 0, QC_FP8_ROWWISE = 1, QC_QSGD = 2, QC_SIGN = 3, QC_TERNARY = 4 };
+enum qc_format {
+    QC_UNIFORM = 0,
+    QC_FP8_ROWWISE = 1,
+    QC_QSGD = 2,
+    QC_SIGN = 3,
+    QC_TERNARY = 4,
+    QC_INT8_SHARED = 5
+};
 enum qc_dtype { QC_F32 = 0, QC_BF16 = 1 };
 
 #define QC_MIN_BUCKET 64
@@ -205,7 +212,9 @@ int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t b
  *          QC_FP8_ROWWISE: group = dim, scale per row, zero unused;
  *          QC_QSGD: bits = 16 (levels), scale = the norm array, zero unused;
  *          QC_SIGN: bits = 1, scale per bucket, zero unused;
- *          QC_TERNARY: bits = 2, scale per bucket, zero unused.
+ *          QC_TERNARY: bits = 2, scale per bucket, zero unused;
+ *          QC_INT8_SHARED: bits = 8, scale per bucket (the shared one), zero
+ *          unused (qc_dequant_accumulate rejects it: use qc_sum_int8_shared).
  *   codes  the payload, read.   out  fp32[n], written.
  * DQ is the formula stated for the matching encoder.
  * Errors: ARG (NULL pointer, n < 0, bad group, n % dim != 0 for FP8),
@@ -242,6 +251,71 @@ int qc_dequant_accumulate(int32_t fmt, const void* codes, const float* scale, co
                           qc_stream_t stream);
 
 /*
+ * Shared-scale INT8 ("distributed quantization": "Quantization for
+ * Communication", section "Quantization-Aware All-Reduce" -- quantize
+ * locally, reduce the quantized data, dequantize after the reduction, with
+ * scale and zero point coordinated across processes; section "Practical
+ * Considerations" -- mismatched parameters give wrong results; "Gradient
+ * Compression and Quantised Collectives", section "Why sparsification
+ * fights the all-reduce" -- compressed forms that add directly).
+ *
+ * The workers agree one scale per bucket before encoding: each computes its
+ * per-bucket max |v| (qc_bucket_absmax), the maxima are combined with max
+ * over workers (what an all-reduce with max computes; qc_absmax_combine
+ * combines m arrays held on one device), and every worker encodes with
+ * scale = amax/127 (qc_encode_int8_shared).  Codes are symmetric int8 in
+ * [-127, 127] with no zero point, so the workers' codes add exactly as
+ * integers in any order, and the receiver dequantizes the sum once
+ * (qc_sum_int8_shared).  Payload: one int8 per element, 16-byte padded
+ * (qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8)); qc_decode decodes one.
+ */
+
+/*
+ * amax[k] = max |x[i] + ef[i]| over bucket k (ef may be NULL: max |x[i]|).
+ *   x, ef  fp32[n], read.   amax  fp32[nb], written (>= +0).
+ * Errors: ARG (NULL x/amax, n < 0, bad bucket), ALIGN.
+ */
+int qc_bucket_absmax(const float* x, const float* ef, int64_t n, int32_t bucket, float* amax,
+                     qc_stream_t stream);
+
+/*
+ * out[k] = max over w of amax[w * nb + k] for m arrays of nb values stored
+ * back to back, taken in worker order with "replace when greater".
+ *   amax  fp32[m * nb], read.   out  fp32[nb], written (may not alias amax).
+ * Errors: ARG (NULL pointer, m outside [1, QC_MAX_WORKERS], nb < 0), ALIGN.
+ */
+int qc_absmax_combine(const float* amax, int32_t m, int64_t nb, float* out, qc_stream_t stream);
+
+/*
+ * Encode with the agreed maximum: per bucket k, s = amax[k] / 127; with
+ * v = x + ef (or x), code = rint(v / s) clamped to [-127, 127] (0 when
+ * s == 0); DQ = code * s; with ef: ef = v - DQ.  scale[k] = s is the same
+ * on every worker that used the same amax.
+ *   amax   fp32[nb], read (e.g. from qc_absmax_combine).
+ *   codes  qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8) bytes, written.
+ *   scale  fp32[nb], written.
+ * Errors: ARG (NULL x/amax/codes/scale, n < 0, bad bucket), ALIGN.
+ */
+int qc_encode_int8_shared(const float* x, float* ef, int64_t n, int32_t bucket, const float* amax,
+                          uint8_t* codes, float* scale, qc_stream_t stream);
+
+/*
+ * Receive side: t[i] = (accumulate ? isum[i] : 0) + c_0[i] + ... + c_{m-1}[i]
+ * over m shared-scale payloads stored back to back (payload w at
+ * w * qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8)); an exact integer sum.
+ * If isum is non-NULL it receives t; if out is non-NULL it receives
+ * (float)t[i] * scale[i / bucket] (one rounding).  The caller keeps |t|
+ * below 2^31 (127 * workers summed so far).
+ *   codes  m payloads, read.   scale  fp32[nb] (the shared scale), read if out.
+ *   isum   int32[n], read if accumulate, written; or NULL.
+ *   out    fp32[n], written; or NULL.  isum and out may not both be NULL.
+ * Errors: ARG (NULL codes, isum and out both NULL, accumulate without isum,
+ *         out without scale, bad m/n/bucket), ALIGN.
+ */
+int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucket, const float* scale,
+                       int32_t* isum, int32_t accumulate, float* out, qc_stream_t stream);
+
+/*
  * signSGD aggregation by majority vote ("Quantization for Communication",
  * section "Quantized SGD Algorithms", SignSGD; "Gradient Compression and
  * Quantised Collectives", section "Why sparsification fights the
@@ -259,7 +333,8 @@ int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_
                      qc_stream_t stream);
 
 /*
- * Bytes of one payload of n elements: the code bytes (n for INT8/FP8,
+ * Bytes of one payload of n elements: the code bytes (n for INT8/FP8 and
+ * shared-scale INT8,
  * 4*ceil(n/8) for 4-bit formats, 4*ceil(n/16) for 2-bit formats,
  * 4*ceil(n/32) for sign) rounded up to 16.
  * `group` is accepted for symmetry and does not change the size.  Returns

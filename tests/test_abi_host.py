@@ -49,6 +49,7 @@ def test_payload_bytes_matches_oracle(qc, ora):
         assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 4) == ora.payload_bytes(ora.UNIFORM, n, 4)
         assert qc.qc_payload_bytes(qc.QC_UNIFORM, n, 64, 2) == ora.payload_bytes(ora.UNIFORM, n, 2)
         assert qc.qc_payload_bytes(qc.QC_TERNARY, n, 64, 2) == ora.payload_bytes(ora.TERNARY, n, 2)
+        assert qc.qc_payload_bytes(qc.QC_INT8_SHARED, n, 64, 8) == ora.payload_bytes(ora.INT8_SHARED, n, 8)
         assert qc.qc_payload_bytes(qc.QC_FP8_ROWWISE, n, 4, 8) == ora.payload_bytes(ora.FP8_ROWWISE, n)
         assert qc.qc_payload_bytes(qc.QC_QSGD, n, 512, 16) == ora.payload_bytes(ora.QSGD, n, 4)
         assert qc.qc_payload_bytes(qc.QC_SIGN, n, 4096, 1) == ora.payload_bytes(ora.SIGN, n, 1)
@@ -193,6 +194,46 @@ def test_dequant_accumulate_errors(qc):
     assert call(qc, f, U, A, A, A, 4, 100, 64, 8, MIS, 0, NULL, NULL, NULL, None) == qc.QC_ERR_ALIGN
     assert call(qc, f, U, A, A, A, 4, 100, 64, 8, A, 0, A, A, MIS, None) == qc.QC_ERR_ALIGN
     assert call(qc, f, U, NULL, NULL, NULL, 4, 0, 64, 8, NULL, 0, NULL, NULL, NULL, None) == qc.QC_OK
+
+
+def test_shared_scale_errors(qc):
+    f = "qc_bucket_absmax"
+    assert call(qc, f, A, A, -1, 512, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 100, 500, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, NULL, A, 100, 512, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 100, 512, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, MIS, 100, 512, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, NULL, 0, 512, NULL, None) == qc.QC_OK
+    f = "qc_absmax_combine"
+    assert call(qc, f, A, 0, 10, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 65536, 10, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 2, -1, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, NULL, 2, 10, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 2, 10, MIS, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, 2, 0, NULL, None) == qc.QC_OK
+    f = "qc_encode_int8_shared"
+    ok = (A, A, 1000, 512, A, A, A, None)
+    for pos in (0, 4, 5, 6):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    for pos in (0, 1, 4, 5, 6):
+        args = list(ok)
+        args[pos] = MIS
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    assert call(qc, f, A, A, 1000, 96, A, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, NULL, NULL, 0, 512, NULL, NULL, NULL, None) == qc.QC_OK
+    f = "qc_sum_int8_shared"
+    assert call(qc, f, A, 0, 100, 512, A, A, 0, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 3, 100, 512, A, NULL, 0, NULL, None) == qc.QC_ERR_ARG   # no output
+    assert call(qc, f, A, 3, 100, 512, A, NULL, 1, A, None) == qc.QC_ERR_ARG      # accumulate needs isum
+    assert call(qc, f, A, 3, 100, 512, NULL, A, 0, A, None) == qc.QC_ERR_ARG      # out needs scale
+    assert call(qc, f, NULL, 3, 100, 512, A, A, 0, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, 3, 100, 512, A, MIS, 0, A, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, 3, 0, 512, NULL, A, 0, NULL, None) == qc.QC_OK
+    # the fp32 accumulator does not take shared-scale payloads
+    assert call(qc, "qc_dequant_accumulate", qc.QC_INT8_SHARED, A, A, NULL, 4, 100, 64, 8, A, 0, NULL, NULL,
+                NULL, None) == qc.QC_ERR_UNSUPPORTED
 
 
 def test_majority_vote_errors(qc):

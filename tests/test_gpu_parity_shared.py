@@ -1,0 +1,218 @@
+"""GPU parity for shared-scale INT8 ("distributed quantization"): the
+per-bucket max statistic, the max-combine over workers, the encoder with
+the agreed scale and error feedback, its decoder, and the exact integer sum
+over workers with its single dequantization -- each called through the C
+ABI and compared bit for bit with the CPU oracle on the same seeded inputs,
+at sizes spanning several tiles with ragged tails, plus degenerate cases."""
+import numpy as np
+import pytest
+
+from embedding_communication_codecs_amd import synth
+from gpu_util import Out, bits_equal, dev, dev_ef, first_diff, need_gpu, out_f32
+
+pytestmark = pytest.mark.gpu
+
+BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536]
+
+
+@pytest.fixture(scope="module")
+def qc():
+    return need_gpu()
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def out_i32(n):
+    import torch
+
+    t = Out(4 * n)
+    return t, t.t.view(torch.int32)
+
+
+def gpu_absmax(qc, x, ef, bucket):
+    n = x.size
+    amax = out_f32(qc.nbuckets(n, bucket))
+    qc.qc_bucket_absmax(dev(x), None if ef is None else ef.t, n, bucket, amax.t)
+    sync()
+    return amax
+
+
+def gpu_encode(qc, x, ef, bucket, amax):
+    n = x.size
+    codes = Out(qc.payload_bytes(qc.QC_INT8_SHARED, n, bucket, 8))
+    scale = out_f32(qc.nbuckets(n, bucket))
+    qc.qc_encode_int8_shared(dev(x), None if ef is None else ef.t, n, bucket, dev(amax), codes.t, scale.t)
+    sync()
+    return codes, scale
+
+
+@pytest.mark.parametrize("bucket", BUCKETS)
+def test_absmax_and_encode_ef_steps(qc, ora, bucket):
+    n = 3 * bucket + 37
+    ef_h = np.zeros(n, np.float32)
+    ef_d = dev_ef(ef_h)
+    for step in range(3):
+        g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=11000 * bucket + step)
+        amax = gpu_absmax(qc, g, ef_d, bucket)
+        want_amax = ora.bucket_absmax(g, ef_h, bucket)
+        assert bits_equal(amax.f32(), want_amax), first_diff(amax.f32(), want_amax)
+        # another worker's larger maximum in some buckets: codes saturate there
+        shared = want_amax.copy()
+        shared[::2] *= np.float32(1.5)
+        codes, scale = gpu_encode(qc, g, ef_d, bucket, shared)
+        p, s = ora.encode_int8_shared(g, ef_h, bucket, shared)
+        assert bits_equal(codes.host(), p), (step, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+        assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    out = out_f32(n)
+    qc.qc_decode(qc.QC_INT8_SHARED, codes.t, scale.t, None, n, bucket, 8, out.t)
+    sync()
+    want = ora.decode_int8_shared(p, s, n, bucket)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 15, 16, 17, 63, 64, 65, 1000, 4096 * 5 + 3])
+def test_encode_ragged_no_ef(qc, ora, n):
+    x = synth.host_normal(n, 1.0, seed=n + 9)
+    amax = gpu_absmax(qc, x, None, 256)
+    assert bits_equal(amax.f32(), ora.bucket_absmax(x, None, 256))
+    codes, scale = gpu_encode(qc, x, None, 256, amax.f32())
+    p, s = ora.encode_int8_shared(x, None, 256, amax.f32())
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s)
+
+
+def test_encode_special_values(qc, ora):
+    """On-grid values, saturation against a smaller agreed maximum, a zero
+    maximum, signed zeros, subnormals and ties at half steps."""
+    B = 64
+    rows = [
+        (np.arange(B, dtype=np.float32) - 32) * np.float32(0.25),               # on a 2^-2 grid
+        np.array([10.0, -10.0, 0.5, -0.5] * 16, np.float32),                   # saturates
+        np.array([1.0, -2.0] * 32, np.float32),                                # zero maximum
+        np.array([-0.0] * 32 + [0.0] * 32, np.float32),
+        np.array([1e-45, -1e-45, 3e-39, -2e-39] * 16, np.float32),
+        (np.arange(B, dtype=np.float32) - 32 + np.float32(0.5)) * np.float32(0.25),  # ties
+    ]
+    x = np.concatenate(rows)
+    amax = np.array([127 * 0.25, 1.0, 0.0, 0.0, 3e-39, 127 * 0.25], np.float32)
+    ef_h = np.zeros(x.size, np.float32)
+    ef_d = dev_ef(ef_h)
+    codes, scale = gpu_encode(qc, x, ef_d, B, amax)
+    p, s = ora.encode_int8_shared(x, ef_h, B, amax)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+    assert bits_equal(scale.f32(), s) and bits_equal(ef_d.f32(), ef_h)
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 64, 1000])
+@pytest.mark.parametrize("nb", [1, 7, 4099])
+def test_absmax_combine(qc, ora, m, nb):
+    rng = np.random.default_rng(m * 31 + nb)
+    a = np.abs(rng.standard_normal(m * nb)).astype(np.float32)
+    a[::5] = 0.0
+    out = out_f32(nb)
+    qc.qc_absmax_combine(dev(a), m, nb, out.t)
+    sync()
+    want = ora.absmax_combine(a, m, nb)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
+def make_workers(qc, ora, m, n, bucket, seed):
+    """m workers agree a scale (oracle statistics), encode on the host."""
+    xs = [synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=seed + w) for w in range(m)]
+    nb = qc.nbuckets(n, bucket)
+    amax = ora.absmax_combine(np.concatenate([ora.bucket_absmax(x, None, bucket) for x in xs]), m, nb)
+    enc = [ora.encode_int8_shared(x, None, bucket, amax) for x in xs]
+    return np.concatenate([p for p, _ in enc]), enc[0][1]
+
+
+@pytest.mark.parametrize("bucket", [64, 512, 2048, 65536])
+@pytest.mark.parametrize("m", [1, 2, 3, 16, 65, 130])
+def test_sum_int8_shared(qc, ora, bucket, m):
+    n = 2 * bucket + 37 if bucket < 65536 else bucket + 37
+    payloads, scale = make_workers(qc, ora, m, n, bucket, seed=12000 + m)
+    want_i, want_o = ora.sum_int8_shared(payloads, m, n, bucket, scale)
+    isum_buf, isum = out_i32(n)
+    out = out_f32(n)
+    codes_d, scale_d = dev(payloads), dev(scale)
+    qc.qc_sum_int8_shared(codes_d, m, n, bucket, scale_d, isum, False, out.t)
+    sync()
+    assert np.array_equal(isum_buf.host().view(np.int32)[:n], want_i)
+    assert bits_equal(out.f32(), want_o), first_diff(out.f32(), want_o)
+    # out only, and isum only
+    out2 = out_f32(n)
+    qc.qc_sum_int8_shared(codes_d, m, n, bucket, scale_d, None, False, out2.t)
+    isum2_buf, isum2 = out_i32(n)
+    qc.qc_sum_int8_shared(codes_d, m, n, bucket, None, isum2, False, None)
+    sync()
+    assert bits_equal(out2.f32(), want_o)
+    assert np.array_equal(isum2_buf.host().view(np.int32)[:n], want_i)
+    # continue from the running sum: twice the workers
+    qc.qc_sum_int8_shared(codes_d, m, n, bucket, scale_d, isum, True, out.t)
+    sync()
+    want_i2, want_o2 = ora.sum_int8_shared(payloads, m, n, bucket, scale, isum=want_i)
+    assert np.array_equal(isum_buf.host().view(np.int32)[:n], want_i2)
+    assert bits_equal(out.f32(), want_o2), first_diff(out.f32(), want_o2)
+
+
+def test_sum_int8_shared_extreme_codes(qc, ora):
+    """Every worker sends +127 or -127 everywhere: the largest sums, and
+    arbitrary codes (-128 included, which the encoder never emits)."""
+    n, B = 5000, 512
+    pb = qc.payload_bytes(qc.QC_INT8_SHARED, n, B, 8)
+    for m, fill in ((300, 127), (300, -127), (17, None)):
+        if fill is None:
+            arena = synth.host_words(m * pb // 4, 5).view(np.uint8).copy()
+        else:
+            arena = np.zeros(m * pb, np.uint8)
+            for w in range(m):
+                arena[w * pb: w * pb + n] = np.uint8(fill & 0xFF)
+        scale = synth.host_normal(qc.nbuckets(n, B), 1.0, seed=m)
+        want_i, want_o = ora.sum_int8_shared(arena, m, n, B, scale)
+        isum_buf, isum = out_i32(n)
+        out = out_f32(n)
+        qc.qc_sum_int8_shared(dev(arena), m, n, B, dev(scale), isum, False, out.t)
+        sync()
+        assert np.array_equal(isum_buf.host().view(np.int32)[:n], want_i)
+        assert bits_equal(out.f32(), want_o), first_diff(out.f32(), want_o)
+
+
+def test_shared_chain_on_gpu_end_to_end(qc, ora):
+    """The whole path on the device: every worker's statistic, the combine,
+    every worker's encode with error feedback, the integer sum -- against
+    the same chain in the oracle."""
+    m, n, B = 8, 3 * 2048 + 11, 2048
+    nb = qc.nbuckets(n, B)
+    import torch
+
+    xs = [synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=13000 + w) for w in range(m)]
+    efs_h = [synth.host_normal(n, 1e-4, seed=13100 + w) for w in range(m)]
+    efs_d = [dev_ef(e) for e in efs_h]
+    stats = torch.empty(m * nb, dtype=torch.float32, device="cuda")
+    for w in range(m):
+        qc.qc_bucket_absmax(dev(xs[w]), efs_d[w].t, n, B, stats[w * nb:(w + 1) * nb])
+    shared = torch.empty(nb, dtype=torch.float32, device="cuda")
+    qc.qc_absmax_combine(stats, m, nb, shared)
+    pb = qc.payload_bytes(qc.QC_INT8_SHARED, n, B, 8)
+    arena = torch.empty(m * pb, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(nb, dtype=torch.float32, device="cuda")
+    for w in range(m):
+        qc.qc_encode_int8_shared(dev(xs[w]), efs_d[w].t, n, B, shared, arena[w * pb:(w + 1) * pb], scale)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    qc.qc_sum_int8_shared(arena, m, n, B, scale, None, False, out)
+    sync()
+    o_stats = np.concatenate([ora.bucket_absmax(xs[w], efs_h[w], B) for w in range(m)])
+    o_shared = ora.absmax_combine(o_stats, m, nb)
+    o_enc = [ora.encode_int8_shared(xs[w], efs_h[w], B, o_shared) for w in range(m)]
+    o_arena = np.concatenate([p for p, _ in o_enc])
+    _, o_out = ora.sum_int8_shared(o_arena, m, n, B, o_enc[0][1])
+    assert bits_equal(stats.cpu().numpy(), o_stats)
+    assert bits_equal(shared.cpu().numpy(), o_shared)
+    assert bits_equal(arena.cpu().numpy(), o_arena)
+    for w in range(m):
+        assert bits_equal(efs_d[w].f32(), efs_h[w])
+    assert bits_equal(out.cpu().numpy(), o_out), first_diff(out.cpu().numpy(), o_out)
