@@ -311,3 +311,42 @@ def sum_int8_shared(payloads, m: int, n: int, bucket: int, scale, isum=None):
     lib().qco_sum_int8_shared(_p(payloads), m, n, bucket, _p(_f32(scale)), _p(acc), 0 if isum is None else 1,
                               _p(out))
     return acc, out
+
+
+# -------------------------------------------------- bucketing front-end
+# [GCQC, "When it breaks": compression is per-tensor and small tensors
+# dominate the launch cost; bucketing many small tensors into one buffer is
+# what makes the exchange efficient.]  Reading: the tensors are
+# concatenated in list order into one buffer, which is then encoded (or
+# decoded and split back) exactly as a single buffer is.
+
+
+def concat(tensors):
+    return np.concatenate([np.asarray(t, dtype=np.float32).ravel() for t in tensors])
+
+
+def encode_uniform_multi(tensors, ef, bucket: int, bits: int):
+    return encode_uniform(concat(tensors), ef, bucket, bits)
+
+
+def decode_flat(fmt: int, payload, scale, zero, n: int, group: int, bits: int):
+    """Any format's decoder on one payload of n elements."""
+    if fmt == UNIFORM:
+        return decode_uniform(payload, scale, zero, n, group, bits)
+    if fmt == FP8_ROWWISE:
+        return decode_fp8_rowwise(payload, scale, n // group, group)
+    if fmt == QSGD:
+        return decode_qsgd(payload, scale, n, group)
+    if fmt == SIGN:
+        return decode_sign(payload, scale, n, group)
+    if fmt == TERNARY:
+        return decode_ternary(payload, scale, n, group)
+    if fmt == INT8_SHARED:
+        return decode_int8_shared(payload, scale, n, group)
+    raise ValueError(fmt)
+
+
+def decode_multi(fmt: int, payload, scale, zero, sizes, group: int, bits: int):
+    """The decoded concatenation split back into tensors of `sizes`."""
+    flat = decode_flat(fmt, payload, scale, zero, int(sum(sizes)), group, bits)
+    return np.split(flat, np.cumsum(sizes)[:-1])
