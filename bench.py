@@ -18,7 +18,11 @@ feedback), TernGrad (buckets of 512, error feedback), shared-scale INT8
 (the per-bucket max statistic and the encode with an agreed maximum, error
 feedback), their decoders, and the receive-side sums of 64 workers'
 payloads of 2^26: TernGrad, 2-bit (requantized to 2 bits in the same
-pass) and shared-scale INT8 (an exact integer sum, dequantized once).  They are reported
+pass) and shared-scale INT8 (an exact integer sum, dequantized once); and
+the bucketing front-end on the parameter list of a 24-layer, width-1024
+transformer (288 tensors, 302M fp32): INT8 + EF of the whole list in one
+launch, the same tensors encoded one launch per tensor, and the decode back
+into the list.  They are reported
 under `extensions`, in the same form as `ops`.
 
 Encoders run first and decoders later in the step, so a decoder never
@@ -59,6 +63,16 @@ C5_M, C5_N, C5_B = 64, 1 << 26, 2048
 # low-bit extensions: on the QSGD gradient, and 64 workers' payloads like C5
 X_N, X_B = C3_N, 512
 X_M, X_AN, X_AB = 64, 1 << 26, 2048
+# bucketing front-end: the parameter list of a 24-layer transformer with
+# width 1024 (per layer: qkv weight and bias, output projection weight and
+# bias, two layer norms' weight and bias, two MLP weights and biases)
+T_D, T_L, T_B = 1024, 24, 4096
+
+
+def tensor_list_sizes():
+    d = T_D
+    layer = [3 * d * d, 3 * d, d * d, d, d, d, 4 * d * d, 4 * d, 4 * d * d, d, d, d]
+    return layer * T_L
 
 
 def source_hash() -> str:
@@ -110,13 +124,27 @@ def ext_bytes():
         "shared_absmax": (4 * X_N, 8 * X_N + 4 * nbx),
         "shared_enc": (4 * X_N, 12 * X_N + X_N + 8 * nbx),
         "shared_sum": (4 * X_M * X_AN, X_M * X_AN + 4 * X_AN + 4 * nba),
+        **list_bytes(),
+    }
+
+
+def list_bytes():
+    sizes = tensor_list_sizes()
+    n = sum(sizes)
+    nb = -(-n // T_B)
+    nb_pt = sum(-(-s // T_B) for s in sizes)
+    return {
+        # x + ef read, ef written, INT8 codes + scale/zero written
+        "list_enc": (4 * n, 13 * n + 8 * nb),
+        "list_enc_per_tensor": (4 * n, 13 * n + 8 * nb_pt),
+        "list_dec": (4 * n, n + 8 * nb + 4 * n),
     }
 
 
 ORDER = ["uniform_enc", "qsgd_enc", "fp8_enc", "sign_enc", "acc_requant", "sign_vote", "qsgd_dec",
          "fp8_dec", "sign_dec", "uniform_dec"]
 EXT_ORDER = ["int2_enc", "stoch4_enc", "tern_enc", "shared_absmax", "shared_enc", "acc_tern", "acc_int2_requant",
-             "shared_sum", "int2_dec", "tern_dec"]
+             "shared_sum", "int2_dec", "tern_dec", "list_enc", "list_enc_per_tensor", "list_dec"]
 
 
 # ------------------------------------------------------------- GPU setup
@@ -224,6 +252,28 @@ def setup_ext(qc, synth, torch, st, empty):
         qc.qc_encode_int8_shared(g, None, X_AN, X_AB, st["xs_amax"], st["xs_codes"][w * pbs:(w + 1) * pbs],
                                  st["xs_scale"])
         del g
+    # the transformer parameter list, as separate tensors (views of one
+    # allocation would hide nothing: the kernel only sees pointers)
+    sizes = tensor_list_sizes()
+    st["tl_x"] = [synth.device_normal(sz, 1e-3, 7000 + k, dev) for k, sz in enumerate(sizes)]
+    st["tl_table"] = qc.TensorTable(st["tl_x"])
+    tn = st["tl_table"].n
+    tnb = -(-tn // T_B)
+    st["tl_ef"] = torch.zeros(tn, dtype=F32, device=dev)
+    st["tl_codes"] = empty(qc.payload_bytes(qc.QC_UNIFORM, tn, T_B, 8))
+    st["tl_scale"] = torch.empty(tnb, dtype=F32, device=dev)
+    st["tl_zero"] = torch.empty(tnb, dtype=F32, device=dev)
+    st["tl_out"] = [torch.empty(sz, dtype=F32, device=dev) for sz in sizes]
+    st["tl_out_table"] = qc.TensorTable(st["tl_out"])
+    # per-tensor encoding: each tensor its own payload, scales and residual
+    st["tl_pt"] = []
+    off = 0
+    for k, sz in enumerate(sizes):
+        nbk = -(-sz // T_B)
+        st["tl_pt"].append((st["tl_x"][k], st["tl_ef"][off: off + sz], sz,
+                            empty(qc.payload_bytes(qc.QC_UNIFORM, sz, T_B, 8)),
+                            torch.empty(nbk, dtype=F32, device=dev), torch.empty(nbk, dtype=F32, device=dev)))
+        off += sz
     st["xa_acc"] = torch.empty(X_AN, dtype=F32, device=dev)
     st["xa_rq"] = empty(pbi)
     st["xa_rqs"] = torch.empty(nba, dtype=F32, device=dev)
@@ -267,6 +317,16 @@ def make_ops(qc, st):
                                                        s["x_i8ss"]),
         "shared_sum": lambda: qc.qc_sum_int8_shared(s["xs_codes"], X_M, X_AN, X_AB, s["xs_scale"], None, False,
                                                     s["xa_acc"]),
+        "list_enc": lambda: qc.qc_encode_uniform_multi(s["tl_table"].xs, s["tl_table"].offsets, s["tl_table"].seg_first,
+                                                       s["tl_table"].ntensors,
+                                                       s["tl_table"].n, s["tl_ef"], T_B, 8, s["tl_codes"],
+                                                       s["tl_scale"], s["tl_zero"]),
+        "list_enc_per_tensor": lambda: [qc.qc_encode_uniform(x, e, sz, T_B, 8, c, sc, z)
+                                        for x, e, sz, c, sc, z in s["tl_pt"]],
+        "list_dec": lambda: qc.qc_decode_multi(qc.QC_UNIFORM, s["tl_codes"], s["tl_scale"], s["tl_zero"],
+                                               s["tl_table"].n, T_B, 8, s["tl_out_table"].xs,
+                                               s["tl_out_table"].offsets, s["tl_out_table"].seg_first,
+                                               s["tl_out_table"].ntensors),
         "acc_tern": lambda: qc.qc_dequant_accumulate(qc.QC_TERNARY, s["xa_t"], s["xa_ts"], None, X_M, X_AN,
                                                      X_AB, 2, s["xa_acc"], False),
         "acc_int2_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["xa_i2"], s["xa_i2s"], s["xa_i2z"],
@@ -519,7 +579,10 @@ def main():
             "accumulate": f"M={C5_M} x {C5_N} INT8, bucket {C5_B}, fused INT8 requant",
             "extensions": (f"outside the step: {X_N} fp32, bucket {X_B}, EF: INT2, stochastic INT4, TernGrad, "
                            f"shared-scale INT8 (max statistic + encode) + decode; M={X_M} x {X_AN}, bucket "
-                           f"{X_AB}: TernGrad sum, INT2 sum + INT2 requant, shared-scale INT8 integer sum"),
+                           f"{X_AB}: TernGrad sum, INT2 sum + INT2 requant, shared-scale INT8 integer sum; "
+                           f"tensor list of a {T_L}-layer width-{T_D} transformer ({len(tensor_list_sizes())} "
+                           f"tensors, {sum(tensor_list_sizes())} fp32), INT8 + EF, bucket {T_B}: one launch, "
+                           f"per-tensor launches, decode into the list"),
         },
         "hbm_frac_step": round(sum(sizes[o][1] for o in names) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     QC_ERR_UNSUPPORTED,
     QC_F32,
     QC_FP8_ROWWISE,
+    QC_INDEX_SHIFT,
     QC_INT8_SHARED,
     QC_MAX_BUCKET,
     QC_MAX_WORKERS,
@@ -26,12 +27,14 @@ from .binding import (  # noqa: F401
     QC_TERNARY,
     QC_UNIFORM,
     QcError,
+    TensorTable,
     lib,
     nbuckets,
     payload_bytes,
     qc_absmax_combine,
     qc_bucket_absmax,
     qc_decode,
+    qc_decode_multi,
     qc_dequant_accumulate,
     qc_encode_fp8_rowwise,
     qc_encode_int8_shared,
@@ -40,8 +43,10 @@ from .binding import (  # noqa: F401
     qc_encode_ternary,
     qc_encode_uniform,
     qc_encode_uniform_stochastic,
+    qc_encode_uniform_multi,
     qc_majority_vote,
     qc_payload_bytes,
     qc_status_str,
     qc_sum_int8_shared,
+    qc_tensor_index,
 )

@@ -21,11 +21,14 @@ QC_OK, QC_ERR_ARG, QC_ERR_ALIGN, QC_ERR_UNSUPPORTED, QC_ERR_LAUNCH = 0, 1, 2, 3,
 QC_UNIFORM, QC_FP8_ROWWISE, QC_QSGD, QC_SIGN, QC_TERNARY, QC_INT8_SHARED = 0, 1, 2, 3, 4, 5
 QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
+QC_INDEX_SHIFT = 12
+QC_MAX_LIST_BUCKET = 32768
 
 EXPORTS = (
-    "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_fp8_rowwise", "qc_encode_qsgd",
+    "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_uniform_multi", "qc_encode_fp8_rowwise",
+    "qc_encode_qsgd",
     "qc_encode_ternary", "qc_encode_sign", "qc_bucket_absmax", "qc_absmax_combine", "qc_encode_int8_shared",
-    "qc_sum_int8_shared", "qc_decode", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
+    "qc_sum_int8_shared", "qc_tensor_index", "qc_decode", "qc_decode_multi", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
 
@@ -51,6 +54,9 @@ def lib() -> ctypes.CDLL:
             "qc_encode_uniform": [P, P, I64, I32, I32, P, P, P, P],
             "qc_encode_uniform_stochastic": [P, P, I64, I32, I32, U64, U64, P, P, P, P],
             "qc_encode_ternary": [P, P, I64, I32, U64, U64, P, P, P],
+            "qc_tensor_index": [P, I32, P, P],
+            "qc_encode_uniform_multi": [P, P, P, I32, I64, P, I32, I32, P, P, P, P],
+            "qc_decode_multi": [I32, P, P, P, I64, I32, I32, P, P, P, I32, P],
             "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
             "qc_encode_qsgd": [P, P, I64, I32, I32, U64, U64, P, P, P],
             "qc_encode_sign": [P, I32, P, I64, I32, P, P, P],
@@ -151,6 +157,62 @@ def qc_encode_ternary(x, ef, n, bucket, seed, elem_offset, words, scale, stream=
         _ptr(words, pb, "words"), _ptr(scale, 4 * nb, "scale"), _stream(stream)))
 
 
+class TensorTable:
+    """Device tables describing a list of fp32 GPU tensors as one buffer:
+    `xs` (int64 data pointers), and the bucket plan qc_tensor_index builds
+    on the host, `offsets` (prefix sums of the sizes, length ntensors + 1)
+    and `seg_first`.  Build it once per list layout and reuse it; it keeps
+    the tensors alive."""
+
+    def __init__(self, tensors):
+        import torch
+
+        if not tensors:
+            raise ValueError("empty tensor list")
+        sizes = []
+        for k, t in enumerate(tensors):
+            if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"tensor {k} must be a contiguous float32 GPU tensor")
+            if t.data_ptr() % 4:
+                raise ValueError(f"tensor {k} is not 4-byte aligned")
+            sizes.append(t.numel())
+        import numpy as np
+
+        self.tensors = list(tensors)
+        self.ntensors = len(sizes)
+        self.n = int(sum(sizes))
+        host_sizes = np.array(sizes, dtype=np.int64)
+        offs = np.empty(self.ntensors + 1, dtype=np.int64)
+        nseg = -(-self.n // (1 << QC_INDEX_SHIFT))
+        seg = np.empty(nseg + 1, dtype=np.int32)
+        _check(lib().qc_tensor_index(host_sizes.ctypes.data, self.ntensors, offs.ctypes.data, seg.ctypes.data))
+        dev = tensors[0].device
+        self.xs = torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=dev)
+        self.offsets = torch.from_numpy(offs).to(dev)
+        self.seg_first = torch.from_numpy(seg).to(dev)
+
+
+def _nseg(n):
+    return -(-max(n, 0) // (1 << QC_INDEX_SHIFT)) + 1
+
+
+def qc_tensor_index(sizes, ntensors, offsets, seg_first) -> None:
+    """Host arrays (numpy): sizes int64[ntensors] in, offsets int64[ntensors+1]
+    and seg_first int32[nseg+1] out."""
+    _check(lib().qc_tensor_index(sizes.ctypes.data, ntensors, offsets.ctypes.data, seg_first.ctypes.data))
+
+
+def qc_encode_uniform_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, codes, scale, zero,
+                            stream=None):
+    """xs/offsets/seg_first: device tables (see TensorTable) or raw addresses."""
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in UNIFORM_BITS and n >= 0 else None
+    _check(lib().qc_encode_uniform_multi(
+        _ptr(xs, 8 * max(ntensors, 0), "xs"), _ptr(offsets, 8 * (max(ntensors, 0) + 1), "offsets"),
+        _ptr(seg_first, 4 * _nseg(n), "seg_first"), ntensors, n, _ptr(ef, 4 * n, "ef"), bucket, bits,
+        _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"), _ptr(zero, 4 * nb, "zero"), _stream(stream)))
+
+
 def qc_encode_fp8_rowwise(x, rows, dim, codes, scale, stream=None):
     n = rows * dim
     pb = payload_bytes(QC_FP8_ROWWISE, n, dim, 8) if n >= 0 else None
@@ -182,6 +244,17 @@ def qc_decode(fmt, codes, scale, zero, n, group, bits, out, stream=None):
     _check(lib().qc_decode(
         fmt, _ptr(codes, pb if pb >= 0 else None, "codes"), _ptr(scale, 4 * nb, "scale"),
         _ptr(zero, 4 * nb, "zero"), n, group, bits, _ptr(out, 4 * n, "out"), _stream(stream)))
+
+
+def qc_decode_multi(fmt, codes, scale, zero, n, group, bits, outs, offsets, seg_first, ntensors, stream=None):
+    """outs/offsets/seg_first: device tables (see TensorTable) or raw addresses."""
+    nb = nbuckets(n, group) if n > 0 and group > 0 else 0
+    pb = payload_bytes(fmt, n, group, bits) if n >= 0 else -1
+    _check(lib().qc_decode_multi(
+        fmt, _ptr(codes, pb if pb >= 0 else None, "codes"), _ptr(scale, 4 * nb, "scale"),
+        _ptr(zero, 4 * nb, "zero"), n, group, bits, _ptr(outs, 8 * max(ntensors, 0), "outs"),
+        _ptr(offsets, 8 * (max(ntensors, 0) + 1), "offsets"), _ptr(seg_first, 4 * _nseg(n), "seg_first"),
+        ntensors, _stream(stream)))
 
 
 def qc_dequant_accumulate(fmt, codes, scale, zero, m, n, group, bits, acc, accumulate,

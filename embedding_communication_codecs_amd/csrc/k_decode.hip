@@ -12,6 +12,7 @@
 #include "qc_device.hpp"
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
+#include "qc.h"
 
 namespace qc {
 namespace {
@@ -57,10 +58,81 @@ __device__ __forceinline__ float chunk_value(uint32_t w, int j, float s, float z
     }
 }
 
-template <int F, bool POW2, int U, bool FULL>
+// ------------------------------------------------------------ outputs
+// FlatOut: one contiguous array.  TensorOuts: the concatenation of T output
+// tensors given by a device table of their pointers and the prefix offsets
+// of their sizes (off[0] = 0, off[T] = n): one launch scatters a decoded
+// bucket buffer back into a whole list of tensors.  prepare() is called once
+// per tile with the tile's element range.
+
+struct FlatOut {
+    float* __restrict__ out;
+    __device__ __forceinline__ void prepare(int64_t, int64_t) {}
+    template <bool FULL>
+    __device__ __forceinline__ void store(int64_t i, int64_t n, const float (&o)[4]) const {
+        if (FULL || i + 4 <= n) {
+            st_f4(out + i, f32x4{o[0], o[1], o[2], o[3]});
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (i + j < n) out[i + j] = o[j];
+        }
+    }
+};
+
+// Largest t in [lo, hi] with off[t] <= g (off[lo] <= g is required).
+__device__ __forceinline__ int32_t tensor_of(const int64_t* __restrict__ off, int32_t lo, int32_t hi, int64_t g) {
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= g) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The tensors holding elements [g0, g1): the segment index brackets them
+// (two loads), a short binary search tightens the bracket.  Index values are
+// clamped to [0, T-1].
+__device__ __forceinline__ void tensor_range(const int64_t* __restrict__ off, const int32_t* __restrict__ seg,
+                                             int32_t T, int64_t g0, int64_t g1, int32_t& lo, int32_t& hi) {
+    int32_t a = seg[g0 >> QC_INDEX_SHIFT], b = seg[((g1 - 1) >> QC_INDEX_SHIFT) + 1];
+    a = a < 0 ? 0 : (a > T - 1 ? T - 1 : a);
+    b = b < a ? a : (b > T - 1 ? T - 1 : b);
+    lo = tensor_of(off, a, b, g0);
+    hi = tensor_of(off, lo, b, g1 - 1);
+}
+
+struct TensorOuts {
+    float* const* __restrict__ outs;
+    const int64_t* __restrict__ off;
+    const int32_t* __restrict__ seg;
+    int32_t T;
+    int32_t lo = 0, hi = 0;
+
+    __device__ __forceinline__ void prepare(int64_t g0, int64_t g1) { tensor_range(off, seg, T, g0, g1, lo, hi); }
+
+    template <bool FULL>
+    __device__ __forceinline__ void store(int64_t i, int64_t n, const float (&o)[4]) const {
+        int32_t t = tensor_of(off, lo, hi, i);
+        float* p = outs[t] + (i - off[t]);
+        if ((FULL || i + 4 <= n) && i + 4 <= off[t + 1] && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+            st_f4(p, f32x4{o[0], o[1], o[2], o[3]});
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t g = i + j;
+            if (!FULL && g >= n) break;
+            while (t < hi && g >= off[t + 1]) ++t;
+            if (g >= off[t] && g < off[t + 1]) outs[t][g - off[t]] = o[j];
+        }
+    }
+};
+
+template <int F, bool POW2, int U, bool FULL, class Dst>
 __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
                                             const float* __restrict__ zero, int64_t n, int64_t nchunks,
-                                            int64_t group, int gshift, float* __restrict__ out, int64_t t0) {
+                                            int64_t group, int gshift, Dst& dst, int64_t t0) {
     uint32_t w[U];
     float s[U], z[U];
 #pragma unroll
@@ -84,48 +156,42 @@ __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, c
         float o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = chunk_value<F>(w[u], j, s[u], z[u]);
-        const int64_t i = c << 2;
-        if (FULL || i + 4 <= n) {
-            st_f4(out + i, f32x4{o[0], o[1], o[2], o[3]});
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (i + j < n) out[i + j] = o[j];
-        }
+        dst.template store<FULL>(c << 2, n, o);
     }
 }
 
 // A tile is 256*U chunks.  Tiles wholly inside n (all but at most the last)
 // take the branch-free path, so a thread's U loads issue back to back.
-template <int F, bool POW2, int U>
+template <int F, bool POW2, int U, class Dst>
 __global__ void __launch_bounds__(256)
 k_decode(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-         const float* __restrict__ zero, int64_t n, int64_t group, int gshift, float* __restrict__ out) {
+         const float* __restrict__ zero, int64_t n, int64_t group, int gshift, Dst dst) {
     const int64_t nchunks = (n + 3) >> 2;
     constexpr int64_t TILE = 256 * U;
     for (int64_t t0 = (int64_t)blockIdx.x * TILE; t0 < nchunks; t0 += (int64_t)gridDim.x * TILE) {
-        if ((t0 + TILE) * 4 <= n)
-            decode_tile<F, POW2, U, true>(codes, scale, zero, n, nchunks, group, gshift, out, t0);
+        const bool full = (t0 + TILE) * 4 <= n;
+        dst.prepare(t0 * 4, full ? (t0 + TILE) * 4 : n);
+        if (full)
+            decode_tile<F, POW2, U, true>(codes, scale, zero, n, nchunks, group, gshift, dst, t0);
         else
-            decode_tile<F, POW2, U, false>(codes, scale, zero, n, nchunks, group, gshift, out, t0);
+            decode_tile<F, POW2, U, false>(codes, scale, zero, n, nchunks, group, gshift, dst, t0);
     }
 }
 
-template <int F, bool POW2>
+template <int F, bool POW2, class Dst>
 hipError_t launch(const void* codes, const float* scale, const float* zero, int64_t n, int32_t group,
-                  float* out, hipStream_t stream) {
+                  Dst dst, hipStream_t stream) {
     constexpr int U = 4;
     const int64_t nchunks = (n + 3) / 4;
     const dim3 grid((unsigned)grid_for(nchunks, 256 * U)), block(256);
-    hipLaunchKernelGGL((k_decode<F, POW2, U>), grid, block, 0, stream, (const uint8_t*)codes, scale,
-                       zero, n, (int64_t)group, log2_exact(group), out);
+    hipLaunchKernelGGL((k_decode<F, POW2, U, Dst>), grid, block, 0, stream, (const uint8_t*)codes, scale,
+                       zero, n, (int64_t)group, log2_exact(group), dst);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, const float* zero,
-                         int64_t n, int32_t group, int32_t bits, float* out, hipStream_t stream) {
+template <class Dst>
+hipError_t launch_decode_dst(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                             int64_t n, int32_t group, int32_t bits, Dst out, hipStream_t stream) {
     switch (fmt) {
         case 0:  // uniform
             if (bits == 8) return launch<F_U8, true>(codes, scale, zero, n, group, out, stream);
@@ -144,6 +210,21 @@ hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, con
         default:
             return launch<F_SIGN, true>(codes, scale, zero, n, group, out, stream);
     }
+}
+
+}  // namespace
+
+hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                         int64_t n, int32_t group, int32_t bits, float* out, hipStream_t stream) {
+    return launch_decode_dst(fmt, codes, scale, zero, n, group, bits, FlatOut{out}, stream);
+}
+
+hipError_t launch_decode_multi(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                               int64_t n, int32_t group, int32_t bits, float* const* outs,
+                               const int64_t* offsets, const int32_t* seg_first, int32_t ntensors,
+                               hipStream_t stream) {
+    return launch_decode_dst(fmt, codes, scale, zero, n, group, bits,
+                             TensorOuts{outs, offsets, seg_first, ntensors}, stream);
 }
 
 }  // namespace qc

@@ -7,6 +7,7 @@
 #include "qc_device.hpp"
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
+#include "qc.h"
 
 #include <type_traits>
 
@@ -51,6 +52,100 @@ __device__ __forceinline__ void store_ef4(float* __restrict__ ef, int64_t i, int
     }
 }
 
+// ------------------------------------------------------------- sources
+// Where an encoder reads x from.  FlatX: one contiguous array.  TensorList:
+// the concatenation of T tensors given by a device table of their
+// pointers and the prefix offsets of their sizes (off[0] = 0, off[t+1] =
+// off[t] + size of tensor t, off[T] = n), so one launch encodes a whole
+// list of gradients as if they had been copied into one buffer first.
+// prepare() is called once per bucket with the bucket's element range.
+
+struct FlatX {
+    const float* __restrict__ x;
+    __device__ __forceinline__ void prepare(int64_t, int64_t) {}
+    template <bool FULL, bool EF>
+    __device__ __forceinline__ void load(const float* __restrict__ ef, int64_t i, int64_t n,
+                                         float (&v)[4]) const {
+        load4<FULL, EF>(x, ef, i, n, v);
+    }
+};
+
+// Largest t in [lo, hi] with off[t] <= g (off[lo] <= g is required).  Empty
+// tensors (off[t] == off[t+1]) are skipped by construction.
+__device__ __forceinline__ int32_t tensor_of(const int64_t* __restrict__ off, int32_t lo, int32_t hi, int64_t g) {
+    while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= g) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The tensors holding elements [g0, g1): the segment index brackets them
+// (two loads), a short binary search tightens the bracket.  Index values are
+// clamped to [0, T-1], so a corrupt index cannot send a read outside the
+// tables.
+__device__ __forceinline__ void tensor_range(const int64_t* __restrict__ off, const int32_t* __restrict__ seg,
+                                             int32_t T, int64_t g0, int64_t g1, int32_t& lo, int32_t& hi) {
+    int32_t a = seg[g0 >> QC_INDEX_SHIFT], b = seg[((g1 - 1) >> QC_INDEX_SHIFT) + 1];
+    a = a < 0 ? 0 : (a > T - 1 ? T - 1 : a);
+    b = b < a ? a : (b > T - 1 ? T - 1 : b);
+    lo = tensor_of(off, a, b, g0);
+    hi = tensor_of(off, lo, b, g1 - 1);
+}
+
+struct TensorList {
+    const float* const* __restrict__ xs;
+    const int64_t* __restrict__ off;
+    const int32_t* __restrict__ seg;  // tensor of element j * 2^QC_INDEX_SHIFT (see qc_tensor_index)
+    int32_t T;
+    int32_t lo = 0, hi = 0;  // tensors that hold the current bucket
+
+    __device__ __forceinline__ void prepare(int64_t g0, int64_t g1) {
+        tensor_range(off, seg, T, g0, g1, lo, hi);
+    }
+
+    // x[g] of the concatenation, with t a tensor at or before the one
+    // holding g; reads nothing outside tensor t's [0, size) range.
+    __device__ __forceinline__ float elem(int32_t& t, int64_t g) const {
+        while (t < hi && g >= off[t + 1]) ++t;
+        const int64_t o = off[t];
+        return (g >= o && g < off[t + 1]) ? xs[t][g - o] : 0.0f;
+    }
+
+    template <bool FULL, bool EF>
+    __device__ __forceinline__ void load(const float* __restrict__ ef, int64_t i, int64_t n,
+                                         float (&v)[4]) const {
+        float e[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (EF) {
+            if (FULL || i + 4 <= n) {
+                const f32x4 t = ld_stream_f4(ef + i);
+                e[0] = t.x; e[1] = t.y; e[2] = t.z; e[3] = t.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (i + j < n) e[j] = ef[i + j];
+            }
+        }
+        float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (FULL || i < n) {
+            int32_t t = tensor_of(off, lo, hi, i);
+            const int64_t o = off[t];
+            const float* p = xs[t] + (i - o);
+            if ((FULL || i + 4 <= n) && i + 4 <= off[t + 1] && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+                const f32x4 q = ld_stream_f4(p);
+                x[0] = q.x; x[1] = q.y; x[2] = q.z; x[3] = q.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (FULL || i + j < n) x[j] = elem(t, i + j);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = EF ? e[j] + x[j] : x[j];
+    }
+};
+
 // Store the codes of a lane's chunk (4 elements from index i) into the
 // payload.  8 bits: one 32-bit word per lane; 4 bits: lanes l and l^1 form
 // one word; 2 bits: lanes 4j..4j+3 form one word.  The lanes of a word hold
@@ -89,8 +184,8 @@ __device__ __forceinline__ void chunk_draws(uint64_t g0, uint32_t k0, uint32_t k
 // scale = (max - min) / (2^BITS - 1); t = (v - min) / scale; code = rint(t),
 // or (STOCH) floor(t) + (u < frac(t)); DQ = code*scale + min; ef = v - DQ.
 
-template <class G, int BITS, bool EF, bool STOCH, bool FULL>
-__device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, float* __restrict__ ef,
+template <class G, int BITS, bool EF, bool STOCH, bool FULL, class Src>
+__device__ __forceinline__ void uniform_bucket(Src src, float* __restrict__ ef,
                                                int64_t n, int64_t bk, uint32_t k0, uint32_t k1,
                                                uint64_t elem_offset, uint8_t* __restrict__ codes,
                                                int64_t pbytes, float* __restrict__ scale,
@@ -98,10 +193,11 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
     constexpr int K = G::K, LPB = G::LPB;
     constexpr uint32_t L = (1u << BITS) - 1u;
     const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
+    src.prepare(bk * (int64_t)G::B, FULL ? (bk + 1) * (int64_t)G::B : n);
 
     float v[K][4];
 #pragma unroll
-    for (int k = 0; k < K; ++k) load4<FULL, EF>(x, ef, base + (int64_t)k * LPB * 4, n, v[k]);
+    for (int k = 0; k < K; ++k) src.template load<FULL, EF>(ef, base + (int64_t)k * LPB * 4, n, v[k]);
 
     float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
@@ -161,18 +257,18 @@ __device__ __forceinline__ void uniform_bucket(const float* __restrict__ x, floa
     }
 }
 
-template <class G, int BITS, bool EF, bool STOCH>
+template <class G, int BITS, bool EF, bool STOCH, class Src>
 __global__ void __launch_bounds__(G::THREADS)
-k_enc_uniform(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0,
-              uint32_t k1, uint64_t elem_offset, uint8_t* __restrict__ codes, int64_t pbytes,
-              float* __restrict__ scale, float* __restrict__ zero) {
+k_enc_uniform(Src src, float* __restrict__ ef, int64_t n, int64_t nb, uint32_t k0, uint32_t k1,
+              uint64_t elem_offset, uint8_t* __restrict__ codes, int64_t pbytes, float* __restrict__ scale,
+              float* __restrict__ zero) {
     __shared__ float lds[G::W];
     for (int64_t bk = first_bucket<G>(); bk < nb; bk += bucket_stride<G>()) {
         if ((bk + 1) * (int64_t)G::B <= n)
-            uniform_bucket<G, BITS, EF, STOCH, true>(x, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
+            uniform_bucket<G, BITS, EF, STOCH, true>(src, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
                                                       scale, zero, lds);
         else
-            uniform_bucket<G, BITS, EF, STOCH, false>(x, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
+            uniform_bucket<G, BITS, EF, STOCH, false>(src, ef, n, bk, k0, k1, elem_offset, codes, pbytes,
                                                        scale, zero, lds);
     }
 }
@@ -515,9 +611,10 @@ k_enc_int8_shared(const float* __restrict__ x, float* __restrict__ ef, int64_t n
 // values in registers); larger buckets spread over W waves of K = 8, and
 // K = 16 only where W would otherwise exceed 16 (1024 threads).
 
-template <int E, class F>
+template <int E, int MAXCHUNKS = 16384, class F>
 hipError_t dispatch_bucket(int32_t bucket, F&& f) {
     const int chunks = bucket / E;
+    if (chunks > MAXCHUNKS) return hipErrorInvalidValue;
     switch (chunks) {
         case 8: if constexpr (E == 8) return f(Geom<E, 8, 1, 1>{}); break;
         case 16: return f(Geom<E, 16, 1, 1>{});
@@ -530,7 +627,7 @@ hipError_t dispatch_bucket(int32_t bucket, F&& f) {
         case 2048: return f(Geom<E, 64, 8, 4>{});
         case 4096: return f(Geom<E, 64, 8, 8>{});
         case 8192: return f(Geom<E, 64, 8, 16>{});
-        case 16384: if constexpr (E == 4) return f(Geom<E, 64, 16, 16>{}); break;
+        case 16384: if constexpr (E == 4 && MAXCHUNKS >= 16384) return f(Geom<E, 64, 16, 16>{}); break;
         default: break;
     }
     return hipErrorInvalidValue;
@@ -545,12 +642,23 @@ hipError_t with_flag(bool flag, F&& f) {
     return flag ? f(std::true_type{}) : f(std::false_type{});
 }
 
-hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
-                                 bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
-                                 int64_t payload_bytes, float* scale, float* zero, hipStream_t stream) {
+namespace {
+
+// The tensor-list source is built for buckets up to 32,768 elements: its
+// 65,536-element variant (1,024 threads, 16 chunks per lane) needs more
+// registers than a thread has and spills heavily, and a parity run of it
+// saw a write past the end of a scale/zero array whose cause is not
+// found, so that variant is not compiled and the call is rejected.
+template <class Src>
+constexpr int max_chunks() { return std::is_same<Src, FlatX>::value ? 16384 : 8192; }
+
+template <class Src>
+hipError_t launch_uniform_src(Src src, float* ef, int64_t n, int32_t bucket, int32_t bits, bool stochastic,
+                              uint64_t seed, uint64_t elem_offset, void* codes, int64_t payload_bytes,
+                              float* scale, float* zero, hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    return dispatch_bucket<4>(bucket, [&](auto g) {
+    return dispatch_bucket<4, max_chunks<Src>()>(bucket, [&](auto g) {
         using G = decltype(g);
         const dim3 grid((unsigned)grid_for(nb, G::BPB)), block(G::THREADS);
         return with_flag(ef != nullptr, [&](auto has_ef) {
@@ -558,18 +666,36 @@ hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t b
             return with_flag(stochastic, [&](auto is_stoch) {
                 constexpr bool ST = decltype(is_stoch)::value;
                 if (bits == 8)
-                    hipLaunchKernelGGL((k_enc_uniform<G, 8, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
-                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                    hipLaunchKernelGGL((k_enc_uniform<G, 8, EF, ST, Src>), grid, block, 0, stream, src, ef, n,
+                                       nb, k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
                 else if (bits == 4)
-                    hipLaunchKernelGGL((k_enc_uniform<G, 4, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
-                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                    hipLaunchKernelGGL((k_enc_uniform<G, 4, EF, ST, Src>), grid, block, 0, stream, src, ef, n,
+                                       nb, k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
                 else
-                    hipLaunchKernelGGL((k_enc_uniform<G, 2, EF, ST>), grid, block, 0, stream, x, ef, n, nb,
-                                       k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
+                    hipLaunchKernelGGL((k_enc_uniform<G, 2, EF, ST, Src>), grid, block, 0, stream, src, ef, n,
+                                       nb, k0, k1, elem_offset, (uint8_t*)codes, payload_bytes, scale, zero);
                 return hipGetLastError();
             });
         });
     });
+}
+
+}  // namespace
+
+hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t bucket, int32_t bits,
+                                 bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                                 int64_t payload_bytes, float* scale, float* zero, hipStream_t stream) {
+    return launch_uniform_src(FlatX{x}, ef, n, bucket, bits, stochastic, seed, elem_offset, codes, payload_bytes,
+                              scale, zero, stream);
+}
+
+hipError_t launch_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                       int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
+                                       bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                                       int64_t payload_bytes, float* scale, float* zero, hipStream_t stream) {
+    TensorList src{xs, offsets, seg_first, ntensors};
+    return launch_uniform_src(src, ef, n, bucket, bits, stochastic, seed, elem_offset, codes, payload_bytes, scale,
+                              zero, stream);
 }
 
 hipError_t launch_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,

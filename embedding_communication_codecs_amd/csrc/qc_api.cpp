@@ -15,6 +15,8 @@ namespace {
 using qc::log2_exact;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 
 bool bad_bucket(int32_t b) {
     return b < QC_MIN_BUCKET || b > QC_MAX_BUCKET || (b & (b - 1)) != 0;
@@ -94,6 +96,44 @@ int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t b
                                  float* zero, qc_stream_t stream) {
     return encode_uniform_any(x, ef, n, bucket, bits, true, seed, elem_offset, codes, scale, zero,
                               stream);
+}
+
+int qc_tensor_index(const int64_t* sizes, int32_t ntensors, int64_t* offsets, int32_t* seg_first) {
+    if (!sizes || !offsets || !seg_first || ntensors < 1) return QC_ERR_ARG;
+    offsets[0] = 0;
+    for (int32_t t = 0; t < ntensors; ++t) {
+        if (sizes[t] < 0) return QC_ERR_ARG;
+        offsets[t + 1] = offsets[t] + sizes[t];
+    }
+    const int64_t n = offsets[ntensors];
+    const int64_t nseg = (n + (int64_t(1) << QC_INDEX_SHIFT) - 1) >> QC_INDEX_SHIFT;
+    int32_t t = 0;
+    for (int64_t j = 0; j <= nseg; ++j) {
+        int64_t g = j << QC_INDEX_SHIFT;
+        if (g > n - 1) g = n - 1;
+        if (g < 0) g = 0;
+        // last tensor whose first element is at or below g (skips empty ones)
+        while (t + 1 < ntensors && offsets[t + 1] <= g) ++t;
+        seg_first[j] = t;
+    }
+    return QC_OK;
+}
+
+int qc_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                            int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits, void* codes,
+                            float* scale, float* zero, qc_stream_t stream) {
+    if (n < 0 || ntensors < 1 || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (bits != 8 && bits != 4 && bits != 2) return QC_ERR_UNSUPPORTED;
+    if (bucket > QC_MAX_LIST_BUCKET) return QC_ERR_UNSUPPORTED;
+    if (n == 0) return QC_OK;
+    if (!xs || !offsets || !seg_first || !codes || !scale || !zero) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned8(xs) || misaligned8(offsets) || misaligned4(seg_first) || misaligned(ef) || misaligned(codes) ||
+        misaligned(scale) || misaligned(zero))
+        return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_uniform_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, false, 0,
+                                                    0, codes, qc_payload_bytes(QC_UNIFORM, n, bucket, bits), scale,
+                                                    zero, hs(stream)));
 }
 
 int qc_encode_fp8_rowwise(const float* x, int64_t rows, int32_t dim, uint8_t* codes, float* scale,
@@ -196,6 +236,22 @@ int qc_decode(int32_t fmt, const void* codes, const float* scale, const float* z
     if (misaligned(codes) || misaligned(scale) || misaligned(zero) || misaligned(out))
         return QC_ERR_ALIGN;
     return launched(qc::launch_decode(fmt, codes, scale, zero, n, group, bits, out, hs(stream)));
+}
+
+int qc_decode_multi(int32_t fmt, const void* codes, const float* scale, const float* zero, int64_t n,
+                    int32_t group, int32_t bits, float* const* outs, const int64_t* offsets,
+                    const int32_t* seg_first, int32_t ntensors, qc_stream_t stream) {
+    if (n < 0 || ntensors < 1) return QC_ERR_ARG;
+    const int st = check_format(fmt, n, group, bits, zero, false);
+    if (st != QC_OK) return st;
+    if (n == 0) return QC_OK;
+    if (!codes || !scale || !outs || !offsets || !seg_first) return QC_ERR_ARG;
+    if (ceil_div(n, group) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned8(outs) || misaligned8(offsets) || misaligned4(seg_first) || misaligned(codes) ||
+        misaligned(scale) || misaligned(zero))
+        return QC_ERR_ALIGN;
+    return launched(qc::launch_decode_multi(fmt, codes, scale, zero, n, group, bits, outs, offsets, seg_first,
+                                            ntensors, hs(stream)));
 }
 
 int qc_dequant_accumulate(int32_t fmt, const void* codes, const float* scale, const float* zero,

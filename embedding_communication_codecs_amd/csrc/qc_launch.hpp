@@ -22,6 +22,11 @@ hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t b
                                  bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
                                  int64_t payload_bytes, float* scale, float* zero, hipStream_t stream);
 
+hipError_t launch_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                       int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
+                                       bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
+                                       int64_t payload_bytes, float* scale, float* zero, hipStream_t stream);
+
 hipError_t launch_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
                                  uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,
                                  float* scale, hipStream_t stream);
@@ -39,6 +44,11 @@ hipError_t launch_encode_sign(const void* x, bool bf16, float* ef, int64_t n, in
 
 hipError_t launch_decode(int32_t fmt, const void* codes, const float* scale, const float* zero,
                          int64_t n, int32_t group, int32_t bits, float* out, hipStream_t stream);
+
+hipError_t launch_decode_multi(int32_t fmt, const void* codes, const float* scale, const float* zero,
+                               int64_t n, int32_t group, int32_t bits, float* const* outs,
+                               const int64_t* offsets, const int32_t* seg_first, int32_t ntensors,
+                               hipStream_t stream);
 
 hipError_t launch_dequant_accumulate(int32_t fmt, const void* codes, const float* scale,
                                      const float* zero, int32_t m, int64_t n, int32_t group,

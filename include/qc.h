@@ -117,6 +117,53 @@ int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t b
                                  float* zero, qc_stream_t stream);
 
 /*
+ * Bucketing front-end ("Gradient Compression and Quantised Collectives",
+ * section "When it breaks": compression is per-tensor and small tensors
+ * dominate the launch cost; bucketing many small tensors into one buffer is
+ * what makes the exchange efficient).  Encodes the concatenation of a list
+ * of fp32 tensors, in list order, exactly as qc_encode_uniform encodes that
+ * concatenation held in one buffer, in one launch and without copying the
+ * tensors: buckets run across tensor boundaries; ef, codes, scale and zero
+ * are laid out for the concatenation.
+ *
+ *   xs       device array of ntensors device pointers (tensor t's fp32 data,
+ *            any 4-byte alignment).
+ *   offsets, seg_first
+ *            device copies of the tables qc_tensor_index builds from the
+ *            sizes (the bucket plan: built once per list layout).  They
+ *            cannot be checked on the host: inconsistent tables give wrong
+ *            values (reads stay inside [xs[t], xs[t] + offsets[t+1] -
+ *            offsets[t]) and inside the tables).
+ *   n        total number of elements (offsets[ntensors]).  Other arguments
+ *            as qc_encode_uniform.
+ * Errors: ARG (NULL table/outputs, ntensors < 1, n < 0, bad bucket), ALIGN
+ *         (xs/offsets not 8-byte aligned, seg_first not 4-byte aligned;
+ *         ef/codes/scale/zero not 16-byte aligned), UNSUPPORTED (bits, or
+ *         bucket above QC_MAX_LIST_BUCKET).
+ */
+/*
+ * The bucket plan of a tensor list, on the host (no device work): from
+ * sizes[t] (elements of tensor t, >= 0) it fills
+ *   offsets[0..ntensors]   prefix sums: offsets[0] = 0, offsets[t+1] =
+ *                          offsets[t] + sizes[t]; offsets[ntensors] = n;
+ *   seg_first[0..nseg]     with nseg = ceil(n / 2^QC_INDEX_SHIFT): the
+ *                          tensor holding element min(j << QC_INDEX_SHIFT,
+ *                          n - 1), i.e. the last t with offsets[t] at or
+ *                          below it (0 when n == 0).
+ * The caller copies both to the device for the *_multi calls.
+ * Returns QC_OK, or QC_ERR_ARG for NULL arrays, ntensors < 1 or a negative
+ * size.
+ */
+#define QC_INDEX_SHIFT 12
+/* Largest bucket qc_encode_uniform_multi accepts. */
+#define QC_MAX_LIST_BUCKET 32768
+int qc_tensor_index(const int64_t* sizes, int32_t ntensors, int64_t* offsets, int32_t* seg_first);
+
+int qc_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                            int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits, void* codes,
+                            float* scale, float* zero, qc_stream_t stream);
+
+/*
  * Rowwise FP8 (OCP E4M3FN) for embedding-lookup payloads: one byte per
  * value plus one fp32 scale per row ("Quantized Communication for
  * Distributed Training", sections "Numeric Example" and "Pinterest QComms
@@ -222,6 +269,21 @@ int qc_encode_sign(const void* x, int32_t xtype, float* ef, int64_t n, int32_t b
  */
 int qc_decode(int32_t fmt, const void* codes, const float* scale, const float* zero, int64_t n,
               int32_t group, int32_t bits, float* out, qc_stream_t stream);
+
+/*
+ * qc_decode of a payload whose n elements are the concatenation of a list of
+ * tensors (see qc_encode_uniform_multi): element offsets[t] + j is written
+ * to outs[t][j].  One launch for the whole list.
+ *   outs     device array of ntensors device pointers (fp32, any 4-byte
+ *            alignment); offsets and seg_first as for
+ *            qc_encode_uniform_multi.
+ *   Other arguments as qc_decode.
+ * Errors: as qc_decode, plus ARG for NULL outs/offsets/seg_first or
+ *         ntensors < 1 and ALIGN for misaligned tables.
+ */
+int qc_decode_multi(int32_t fmt, const void* codes, const float* scale, const float* zero, int64_t n,
+                    int32_t group, int32_t bits, float* const* outs, const int64_t* offsets,
+                    const int32_t* seg_first, int32_t ntensors, qc_stream_t stream);
 
 /*
  * Receive-side quantized accumulation in fp32 ("Quantization for

@@ -253,3 +253,66 @@ def test_binding_rejects_undersized_buffers_before_the_library(qc):
     x = torch.zeros(10)
     with pytest.raises(ValueError):
         qc.qc_encode_uniform(x, None, 10, 64, 8, x, x, x, stream=0)
+
+
+def test_tensor_index_plan(qc):
+    """The bucket plan qc_tensor_index builds on the host: prefix offsets,
+    and for each 4096-element segment the tensor holding its first element
+    (empty tensors skipped), checked against numpy's searchsorted."""
+    import numpy as np
+
+    rng = np.random.default_rng(0)
+    shift = qc.QC_INDEX_SHIFT
+    for sizes in ([5], [0, 0, 7, 0], [4096, 4096], [4095, 1, 0, 8192, 3],
+                  list(rng.integers(0, 9000, 300)), list(rng.integers(0, 3, 5000))):
+        sizes = np.array(sizes, dtype=np.int64)
+        n = int(sizes.sum())
+        offs = np.empty(sizes.size + 1, np.int64)
+        nseg = -(-n // (1 << shift))
+        seg = np.empty(nseg + 1, np.int32)
+        qc.qc_tensor_index(sizes, sizes.size, offs, seg)
+        assert offs[0] == 0 and np.array_equal(np.diff(offs), sizes)
+        for j in range(nseg + 1):
+            g = max(0, min(j << shift, n - 1))
+            t = int(np.searchsorted(offs, g, side="right")) - 1
+            t = min(t, sizes.size - 1)
+            if n > 0:
+                assert offs[seg[j]] <= g < offs[seg[j] + 1], (j, g, seg[j])
+                assert seg[j] == t
+    bad = np.array([3, -1], np.int64)
+    with pytest.raises(qc.QcError):
+        qc.qc_tensor_index(bad, 2, np.empty(3, np.int64), np.empty(2, np.int32))
+
+
+def test_multi_entry_point_errors(qc):
+    f = "qc_encode_uniform_multi"
+    ok = (A, A, A, 5, 1000, A, 512, 8, A, A, A, None)
+    for pos in (0, 1, 2, 8, 9, 10):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    args = list(ok)
+    args[3] = 0
+    assert call(qc, f, *args) == qc.QC_ERR_ARG
+    args = list(ok)
+    args[7] = 3
+    assert call(qc, f, *args) == qc.QC_ERR_UNSUPPORTED
+    args = list(ok)
+    args[6] = 65536   # above QC_MAX_LIST_BUCKET
+    assert call(qc, f, *args) == qc.QC_ERR_UNSUPPORTED
+    for pos, bad in ((0, A + 4), (1, A + 4), (2, A + 2), (5, MIS), (8, MIS)):
+        args = list(ok)
+        args[pos] = bad
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    f = "qc_decode_multi"
+    ok = (0, A, A, A, 1000, 512, 8, A, A, A, 5, None)
+    for pos in (7, 8, 9):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    args = list(ok)
+    args[10] = 0
+    assert call(qc, f, *args) == qc.QC_ERR_ARG
+    args = list(ok)
+    args[9] = A + 2
+    assert call(qc, f, *args) == qc.QC_ERR_ALIGN
