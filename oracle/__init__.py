@@ -79,6 +79,9 @@ def lib():
         L.qco_encode_int8_shared.argtypes = [P, P, I64, I32, P, P, P]
         L.qco_decode_int8_shared.argtypes = [P, P, I64, I32, P]
         L.qco_sum_int8_shared.argtypes = [P, I32, I64, I32, P, P, I32, P]
+        L.qco_encode_topk.argtypes = [P, P, I64, I32, I32, P, P]
+        L.qco_decode_topk.argtypes = [P, P, I64, I32, I32, P]
+        L.qco_topk_accumulate.argtypes = [P, P, I32, I64, I32, I32, P, I32]
         _lib = L
     return _lib
 
@@ -311,6 +314,33 @@ def sum_int8_shared(payloads, m: int, n: int, bucket: int, scale, isum=None):
     lib().qco_sum_int8_shared(_p(payloads), m, n, bucket, _p(_f32(scale)), _p(acc), 0 if isum is None else 1,
                               _p(out))
     return acc, out
+
+
+# ----------------------------------------------------------------- top-k
+
+
+def encode_topk(x, ef, bucket: int, k: int):
+    """Returns (values float32[nb*k], indices uint32[nb*k]); ef is updated."""
+    x = _f32(x)
+    ef = _ef(ef)
+    nb = nbuckets(x.size, bucket)
+    values = np.empty(nb * k, dtype=np.float32)
+    indices = np.empty(nb * k, dtype=np.uint32)
+    lib().qco_encode_topk(_p(x), _p(ef), x.size, bucket, k, _p(values), _p(indices))
+    return values, indices
+
+
+def decode_topk(values, indices, n: int, bucket: int, k: int):
+    out = np.empty(n, dtype=np.float32)
+    lib().qco_decode_topk(_p(_f32(values)), _p(np.ascontiguousarray(indices, np.uint32)), n, bucket, k, _p(out))
+    return out
+
+
+def topk_accumulate(values, indices, m: int, n: int, bucket: int, k: int, acc=None):
+    out = np.zeros(n, dtype=np.float32) if acc is None else _f32(acc).copy()
+    lib().qco_topk_accumulate(_p(_f32(values)), _p(np.ascontiguousarray(indices, np.uint32)), m, n, bucket, k,
+                              _p(out), 0 if acc is None else 1)
+    return out
 
 
 # -------------------------------------------------- bucketing front-end

@@ -641,6 +641,112 @@ void qco_sum_int8_shared(const uint8_t* payloads, int32_t m, int64_t n, int32_t 
     }
 }
 
+/* ------------------------------------------------------------------ */
+/* top-k sparsification  [GQC, "Quantization Schemes": Top-K             */
+/*   sparsification; GCQC, opening section: only the largest-magnitude  */
+/*   coordinates; GCQC, "Why sparsification fights the all-reduce":     */
+/*   index-value pairs; GCQC, "Error feedback is the component that     */
+/*   makes it work"]                                                    */
+/* ------------------------------------------------------------------ */
+/* Readings: the selection is made per bucket, like every other statistic
+ * here; a bucket sends k_b = min(k, count) coordinates, those of largest
+ * |v| (v = x + ef), comparing the fp32 magnitude (the bit pattern with the
+ * sign cleared); equal magnitudes go to the smaller index, so the chosen set
+ * is unique.  Each chosen coordinate travels as (index inside the bucket,
+ * fp32 value), in ascending index order; the residual is v - sent, i.e. v
+ * for unsent coordinates and 0 for sent ones.  The receiver's sum of
+ * several workers' pairs is a sparse sum: each pair is added to the dense
+ * accumulator in worker order (elements no pair touches are left as they
+ * are). */
+
+typedef struct { uint32_t key; uint32_t idx; } topk_item;
+
+static int topk_order(const void* a, const void* b)
+{
+    const topk_item* p = (const topk_item*)a;
+    const topk_item* q = (const topk_item*)b;
+    if (p->key != q->key)
+        return p->key > q->key ? -1 : 1;   /* larger magnitude first */
+    return p->idx < q->idx ? -1 : (p->idx > q->idx ? 1 : 0);  /* then smaller index */
+}
+
+void qco_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k,
+                     float* values, uint32_t* indices)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    float* v = (float*)malloc((size_t)bucket * sizeof(float));
+    topk_item* items = (topk_item*)malloc((size_t)bucket * sizeof(topk_item));
+    uint8_t* chosen = (uint8_t*)malloc((size_t)bucket);
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = b * bucket;
+        const int64_t cnt = (lo + bucket <= n) ? bucket : n - lo;
+        const int64_t kb = k < cnt ? k : cnt;
+        for (int64_t j = 0; j < cnt; ++j) {
+            v[j] = ef ? ef[lo + j] + x[lo + j] : x[lo + j];
+            items[j].key = f32_bits(v[j]) & 0x7FFFFFFFu;
+            items[j].idx = (uint32_t)j;
+            chosen[j] = 0;
+        }
+        qsort(items, (size_t)cnt, sizeof(topk_item), topk_order);
+        for (int64_t r = 0; r < kb; ++r)
+            chosen[items[r].idx] = 1;
+        int64_t slot = b * (int64_t)k;
+        for (int64_t j = 0; j < cnt; ++j) {
+            if (chosen[j]) {
+                values[slot] = v[j];
+                indices[slot] = (uint32_t)j;
+                ++slot;
+            }
+            if (ef)
+                ef[lo + j] = v[j] - (chosen[j] ? v[j] : 0.0f);
+        }
+        for (; slot < (b + 1) * (int64_t)k; ++slot) {
+            values[slot] = 0.0f;
+            indices[slot] = 0xFFFFFFFFu;
+        }
+    }
+    free(v);
+    free(items);
+    free(chosen);
+}
+
+void qco_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket,
+                     int32_t k, float* out)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = 0.0f;
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t cnt = (b * bucket + bucket <= n) ? bucket : n - b * bucket;
+        for (int64_t j = 0; j < k; ++j) {
+            const uint32_t idx = indices[b * k + j];
+            if ((int64_t)idx < cnt)
+                out[b * bucket + idx] = values[b * k + j];
+        }
+    }
+}
+
+void qco_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n,
+                         int32_t bucket, int32_t k, float* acc, int32_t accumulate)
+{
+    const int64_t nb = ceil_div(n, bucket);
+    if (!accumulate)
+        for (int64_t i = 0; i < n; ++i)
+            acc[i] = 0.0f;
+    for (int32_t w = 0; w < m; ++w) {
+        const float* vw = values + (int64_t)w * nb * k;
+        const uint32_t* iw = indices + (int64_t)w * nb * k;
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t cnt = (b * bucket + bucket <= n) ? bucket : n - b * bucket;
+            for (int64_t j = 0; j < k; ++j) {
+                const uint32_t idx = iw[b * k + j];
+                if ((int64_t)idx < cnt)
+                    acc[b * bucket + idx] = acc[b * bucket + idx] + vw[b * k + j];
+            }
+        }
+    }
+}
+
 float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,
                      const float* zero, int64_t i, int32_t group, int32_t bits)
 {

@@ -116,6 +116,23 @@ void qco_decode_int8_shared(const uint8_t* payload, const float* scale, int64_t 
 void qco_sum_int8_shared(const uint8_t* payloads, int32_t m, int64_t n, int32_t bucket,
                          const float* scale, int32_t* isum, int32_t accumulate, float* out);
 
+/* Top-k sparsification with error feedback: per bucket, the k_b = min(k,
+ * count) coordinates of largest |v| (ties to the smaller index) are sent as
+ * (local index, value) pairs in ascending index order, into slots
+ * [b*k, b*k + k_b) of values/indices; slots past k_b hold index 0xFFFFFFFF
+ * and value +0.  ef (may be NULL) keeps every unsent coordinate whole.
+ *   qco_decode_topk:     out = 0 everywhere, then out[b*bucket + idx] = value.
+ *   qco_topk_accumulate: acc = (accumulate ? acc : +0); then for each worker
+ *                        in order and each valid pair in slot order,
+ *                        acc[b*bucket + idx] = acc[...] + value.  Worker w's
+ *                        pairs start at w * nb * k. */
+void qco_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k,
+                     float* values, uint32_t* indices);
+void qco_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket,
+                     int32_t k, float* out);
+void qco_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n,
+                         int32_t bucket, int32_t k, float* acc, int32_t accumulate);
+
 /* Element i of a payload decoded to fp32, for any format. */
 float qco_decode_one(int32_t fmt, const uint8_t* payload, const float* scale,
                      const float* zero, int64_t i, int32_t group, int32_t bits);

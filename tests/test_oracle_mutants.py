@@ -24,6 +24,7 @@ PIN_MODULES = [
     _load("oracle_pins_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins.py")),
     _load("oracle_pins_stochastic_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_stochastic.py")),
     _load("oracle_pins_shared_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_shared.py")),
+    _load("oracle_pins_topk_for_mutants", os.path.join(ROOT, "tests", "test_oracle_pins_topk.py")),
 ]
 
 
@@ -114,6 +115,21 @@ MUTANTS = [
      "out[i] = (float)payload[i] * scale[i / bucket];", ["test_int8_shared_on_grid_is_exact"]),
     ("shared_ef_not_updated", "ef[i] = v - (float)q * sc;", "ef[i] = v;",
      ["test_int8_shared_on_grid_is_exact", "test_int8_shared_error_bound_and_feedback"]),
+    ("topk_ties_to_larger_index", "return p->idx < q->idx ? -1 : (p->idx > q->idx ? 1 : 0);",
+     "return p->idx > q->idx ? -1 : (p->idx < q->idx ? 1 : 0);", ["test_brute_force_selection_tiny",
+                                                                    "test_closed_forms"]),
+    ("topk_smallest_first", "return p->key > q->key ? -1 : 1;", "return p->key < q->key ? -1 : 1;",
+     ["test_brute_force_selection_tiny", "test_closed_forms"]),
+    ("topk_key_keeps_sign", "items[j].key = f32_bits(v[j]) & 0x7FFFFFFFu;", "items[j].key = f32_bits(v[j]);",
+     ["test_brute_force_selection_tiny"]),
+    ("topk_one_fewer", "const int64_t kb = k < cnt ? k : cnt;", "const int64_t kb = k - 1 < cnt ? k - 1 : cnt;",
+     ["test_brute_force_selection_tiny", "test_closed_forms"]),
+    ("topk_ef_keeps_sent", "ef[lo + j] = v[j] - (chosen[j] ? v[j] : 0.0f);", "ef[lo + j] = v[j];",
+     ["test_closed_forms", "test_error_feedback_keeps_everything"]),
+    ("topk_decode_drops_bucket_offset", "                out[b * bucket + idx] = values[b * k + j];",
+     "                out[idx] = values[b * k + j];", ["test_decode_places_values"]),
+    ("topk_acc_skips_first_worker", "for (int32_t w = 0; w < m; ++w) {\n        const float* vw",
+     "for (int32_t w = 1; w < m; ++w) {\n        const float* vw", ["test_sum_of_sparse_workers"]),
 ]
 
 
@@ -148,6 +164,8 @@ def _run_pin(fn, mod, rocrand_philox):
         variants = [{"fmt": f} for f in ("fp8", "qsgd", "sign", "int4")]
     if "with_ef" in sig.parameters:
         variants = [{"with_ef": False}, {"with_ef": True}]
+    if "k" in sig.parameters:
+        variants = [{"k": 1}, {"k": 3}, {"k": 64}]
     for v in variants:
         fn(**kw, **v)
 
