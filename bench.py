@@ -22,7 +22,9 @@ pass) and shared-scale INT8 (an exact integer sum, dequantized once); and
 the bucketing front-end on the parameter list of a 24-layer, width-1024
 transformer (288 tensors, 302M fp32): INT8 + EF of the whole list in one
 launch, the same tensors encoded one launch per tensor, and the decode back
-into the list.  They are reported
+into the list; top-k sparsification (16 of every 16,384 coordinates, error
+feedback) of the 1e9 gradient, its decode, and the sum of 64 workers'
+top-k payloads of 2^26.  They are reported
 under `extensions`, in the same form as `ops`.
 
 Encoders run first and decoders later in the step, so a decoder never
@@ -67,6 +69,8 @@ X_M, X_AN, X_AB = 64, 1 << 26, 2048
 # width 1024 (per layer: qkv weight and bias, output projection weight and
 # bias, two layer norms' weight and bias, two MLP weights and biases)
 T_D, T_L, T_B = 1024, 24, 4096
+# top-k: density about 1/1000 (16 of every 16,384 coordinates)
+K_B, K_K = 16384, 16
 
 
 def tensor_list_sizes():
@@ -125,6 +129,21 @@ def ext_bytes():
         "shared_enc": (4 * X_N, 12 * X_N + X_N + 8 * nbx),
         "shared_sum": (4 * X_M * X_AN, X_M * X_AN + 4 * X_AN + 4 * nba),
         **list_bytes(),
+        **topk_bytes(),
+    }
+
+
+def topk_bytes():
+    pairs = 8 * K_K * -(-X_N // K_B)
+    pairs_w = 8 * K_K * (X_AN // K_B)
+    return {
+        # x + ef read, ef written, (index, value) pairs written
+        "topk_enc": (4 * X_N, 12 * X_N + pairs),
+        # pairs read, the dense vector written (zeros and values)
+        "topk_dec": (4 * X_N, pairs + 4 * X_N),
+        # 64 workers' pairs read; the accumulator zeroed, then read and
+        # written where pairs land
+        "topk_sum": (4 * X_M * X_AN, X_M * pairs_w + 4 * X_AN + X_M * pairs_w),
     }
 
 
@@ -144,7 +163,8 @@ def list_bytes():
 ORDER = ["uniform_enc", "qsgd_enc", "fp8_enc", "sign_enc", "acc_requant", "sign_vote", "qsgd_dec",
          "fp8_dec", "sign_dec", "uniform_dec"]
 EXT_ORDER = ["int2_enc", "stoch4_enc", "tern_enc", "shared_absmax", "shared_enc", "acc_tern", "acc_int2_requant",
-             "shared_sum", "int2_dec", "tern_dec", "list_enc", "list_enc_per_tensor", "list_dec"]
+             "shared_sum", "int2_dec", "tern_dec", "list_enc", "list_enc_per_tensor", "list_dec",
+             "topk_enc", "topk_sum", "topk_dec"]
 
 
 # ------------------------------------------------------------- GPU setup
@@ -274,6 +294,18 @@ def setup_ext(qc, synth, torch, st, empty):
                             empty(qc.payload_bytes(qc.QC_UNIFORM, sz, T_B, 8)),
                             torch.empty(nbk, dtype=F32, device=dev), torch.empty(nbk, dtype=F32, device=dev)))
         off += sz
+    # top-k payloads: the 1e9 gradient, and 64 workers of 2^26
+    kslots = -(-X_N // K_B) * K_K
+    st["k_vals"] = torch.empty(kslots, dtype=F32, device=dev)
+    st["k_idx"] = torch.empty(kslots, dtype=torch.int32, device=dev)
+    wslots = (X_AN // K_B) * K_K
+    st["kw_vals"] = torch.empty(X_M * wslots, dtype=F32, device=dev)
+    st["kw_idx"] = torch.empty(X_M * wslots, dtype=torch.int32, device=dev)
+    for w in range(X_M):
+        g = synth.device_outlier_grad(X_AN, 1e-3, 0.01, 100.0, 6000 + w, dev)
+        qc.qc_encode_topk(g, None, X_AN, K_B, K_K, st["kw_vals"][w * wslots:(w + 1) * wslots],
+                          st["kw_idx"][w * wslots:(w + 1) * wslots])
+        del g
     st["xa_acc"] = torch.empty(X_AN, dtype=F32, device=dev)
     st["xa_rq"] = empty(pbi)
     st["xa_rqs"] = torch.empty(nba, dtype=F32, device=dev)
@@ -327,6 +359,9 @@ def make_ops(qc, st):
                                                s["tl_table"].n, T_B, 8, s["tl_out_table"].xs,
                                                s["tl_out_table"].offsets, s["tl_out_table"].seg_first,
                                                s["tl_out_table"].ntensors),
+        "topk_enc": lambda: qc.qc_encode_topk(s["c3_x"], s["x_ef"], X_N, K_B, K_K, s["k_vals"], s["k_idx"]),
+        "topk_dec": lambda: qc.qc_decode_topk(s["k_vals"], s["k_idx"], X_N, K_B, K_K, s["c3_out"]),
+        "topk_sum": lambda: qc.qc_topk_accumulate(s["kw_vals"], s["kw_idx"], X_M, X_AN, K_B, K_K, s["xa_acc"], False),
         "acc_tern": lambda: qc.qc_dequant_accumulate(qc.QC_TERNARY, s["xa_t"], s["xa_ts"], None, X_M, X_AN,
                                                      X_AB, 2, s["xa_acc"], False),
         "acc_int2_requant": lambda: qc.qc_dequant_accumulate(qc.QC_UNIFORM, s["xa_i2"], s["xa_i2s"], s["xa_i2z"],
@@ -582,7 +617,8 @@ def main():
                            f"{X_AB}: TernGrad sum, INT2 sum + INT2 requant, shared-scale INT8 integer sum; "
                            f"tensor list of a {T_L}-layer width-{T_D} transformer ({len(tensor_list_sizes())} "
                            f"tensors, {sum(tensor_list_sizes())} fp32), INT8 + EF, bucket {T_B}: one launch, "
-                           f"per-tensor launches, decode into the list"),
+                           f"per-tensor launches, decode into the list; top-k {K_K} of every {K_B} + EF on the "
+                           f"{X_N} gradient, its decode, and the sparse sum of {X_M} workers x {X_AN}"),
         },
         "hbm_frac_step": round(sum(sizes[o][1] for o in names) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     QC_INDEX_SHIFT,
     QC_INT8_SHARED,
     QC_MAX_BUCKET,
+    QC_MAX_TOPK_BUCKET,
     QC_MAX_WORKERS,
     QC_MIN_BUCKET,
     QC_OK,
@@ -35,12 +36,14 @@ from .binding import (  # noqa: F401
     qc_bucket_absmax,
     qc_decode,
     qc_decode_multi,
+    qc_decode_topk,
     qc_dequant_accumulate,
     qc_encode_fp8_rowwise,
     qc_encode_int8_shared,
     qc_encode_qsgd,
     qc_encode_sign,
     qc_encode_ternary,
+    qc_encode_topk,
     qc_encode_uniform,
     qc_encode_uniform_stochastic,
     qc_encode_uniform_multi,
@@ -49,4 +52,5 @@ from .binding import (  # noqa: F401
     qc_status_str,
     qc_sum_int8_shared,
     qc_tensor_index,
+    qc_topk_accumulate,
 )

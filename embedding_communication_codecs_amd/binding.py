@@ -23,12 +23,14 @@ QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
 QC_INDEX_SHIFT = 12
 QC_MAX_LIST_BUCKET = 32768
+QC_MAX_TOPK_BUCKET = 16384
 
 EXPORTS = (
     "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_uniform_multi", "qc_encode_fp8_rowwise",
     "qc_encode_qsgd",
     "qc_encode_ternary", "qc_encode_sign", "qc_bucket_absmax", "qc_absmax_combine", "qc_encode_int8_shared",
-    "qc_sum_int8_shared", "qc_tensor_index", "qc_decode", "qc_decode_multi", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
+    "qc_sum_int8_shared", "qc_tensor_index", "qc_encode_topk", "qc_decode_topk", "qc_topk_accumulate",
+    "qc_decode", "qc_decode_multi", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
 
@@ -55,6 +57,9 @@ def lib() -> ctypes.CDLL:
             "qc_encode_uniform_stochastic": [P, P, I64, I32, I32, U64, U64, P, P, P, P],
             "qc_encode_ternary": [P, P, I64, I32, U64, U64, P, P, P],
             "qc_tensor_index": [P, I32, P, P],
+            "qc_encode_topk": [P, P, I64, I32, I32, P, P, P],
+            "qc_decode_topk": [P, P, I64, I32, I32, P, P],
+            "qc_topk_accumulate": [P, P, I32, I64, I32, I32, P, I32, P],
             "qc_encode_uniform_multi": [P, P, P, I32, I64, P, I32, I32, P, P, P, P],
             "qc_decode_multi": [I32, P, P, P, I64, I32, I32, P, P, P, I32, P],
             "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
@@ -296,6 +301,26 @@ def qc_sum_int8_shared(codes, m, n, bucket, scale, isum, accumulate, out, stream
         _ptr(codes, max(m, 0) * pb if pb is not None else None, "codes"), m, n, bucket,
         _ptr(scale, 4 * nb, "scale"), _ptr(isum, 4 * max(n, 0), "isum"), 1 if accumulate else 0,
         _ptr(out, 4 * max(n, 0), "out"), _stream(stream)))
+
+
+def qc_encode_topk(x, ef, n, bucket, k, values, indices, stream=None):
+    slots = nbuckets(n, bucket) * k if n > 0 and bucket > 0 and k > 0 else 0
+    _check(lib().qc_encode_topk(_ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, k,
+                                _ptr(values, 4 * slots, "values"), _ptr(indices, 4 * slots, "indices"),
+                                _stream(stream)))
+
+
+def qc_decode_topk(values, indices, n, bucket, k, out, stream=None):
+    slots = nbuckets(n, bucket) * k if n > 0 and bucket > 0 and k > 0 else 0
+    _check(lib().qc_decode_topk(_ptr(values, 4 * slots, "values"), _ptr(indices, 4 * slots, "indices"), n,
+                                bucket, k, _ptr(out, 4 * max(n, 0), "out"), _stream(stream)))
+
+
+def qc_topk_accumulate(values, indices, m, n, bucket, k, acc, accumulate, stream=None):
+    slots = max(m, 0) * (nbuckets(n, bucket) * k if n > 0 and bucket > 0 and k > 0 else 0)
+    _check(lib().qc_topk_accumulate(_ptr(values, 4 * slots, "values"), _ptr(indices, 4 * slots, "indices"), m,
+                                    n, bucket, k, _ptr(acc, 4 * max(n, 0), "acc"), 1 if accumulate else 0,
+                                    _stream(stream)))
 
 
 def qc_majority_vote(words, m, n, out_words, stream=None):

@@ -34,7 +34,7 @@ FLAGS = [
     "-Wno-unused-function",
 ]
 SOURCES = ["k_encode.hip", "k_fp8.hip", "k_decode.hip", "k_accumulate.hip", "k_vote.hip", "k_shared_sum.hip",
-           "qc_api.cpp"]
+           "k_topk.hip", "qc_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -320,6 +320,51 @@ int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucke
                                                scale, isum, accumulate != 0, out, hs(stream)));
 }
 
+namespace {
+
+int check_topk(int64_t n, int32_t bucket, int32_t k) {
+    if (n < 0 || bad_bucket(bucket) || k < 1 || k > bucket) return QC_ERR_ARG;
+    if (bucket > QC_MAX_TOPK_BUCKET) return QC_ERR_UNSUPPORTED;
+    if (ceil_div(n, bucket) * (int64_t)k > (int64_t(1) << 40)) return QC_ERR_ARG;
+    return QC_OK;
+}
+
+}  // namespace
+
+int qc_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k, float* values,
+                   uint32_t* indices, qc_stream_t stream) {
+    const int st = check_topk(n, bucket, k);
+    if (st != QC_OK) return st;
+    if (n == 0) return QC_OK;
+    if (!x || !values || !indices) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned(x) || misaligned(ef) || misaligned4(values) || misaligned4(indices)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_topk(x, ef, n, bucket, k, values, indices, hs(stream)));
+}
+
+int qc_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket, int32_t k,
+                   float* out, qc_stream_t stream) {
+    const int st = check_topk(n, bucket, k);
+    if (st != QC_OK) return st;
+    if (n == 0) return QC_OK;
+    if (!values || !indices || !out) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned4(values) || misaligned4(indices) || misaligned(out)) return QC_ERR_ALIGN;
+    return launched(qc::launch_decode_topk(values, indices, n, bucket, k, out, hs(stream)));
+}
+
+int qc_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n, int32_t bucket,
+                       int32_t k, float* acc, int32_t accumulate, qc_stream_t stream) {
+    if (m < 1 || m > QC_MAX_WORKERS) return QC_ERR_ARG;
+    const int st = check_topk(n, bucket, k);
+    if (st != QC_OK) return st;
+    if (n == 0) return QC_OK;
+    if (!values || !indices || !acc) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned4(values) || misaligned4(indices) || misaligned(acc)) return QC_ERR_ALIGN;
+    return launched(qc::launch_topk_accumulate(values, indices, m, n, bucket, k, acc, accumulate != 0, hs(stream)));
+}
+
 int qc_majority_vote(const uint32_t* words, int32_t m, int64_t n, uint32_t* out_words,
                      qc_stream_t stream) {
     if (n < 0 || m < 1 || m > QC_MAX_WORKERS) return QC_ERR_ARG;

@@ -68,6 +68,15 @@ hipError_t launch_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, in
                                   int64_t payload_bytes, const float* scale, int32_t* isum, bool accumulate,
                                   float* out, hipStream_t stream);
 
+hipError_t launch_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k, float* values,
+                              uint32_t* indices, hipStream_t stream);
+
+hipError_t launch_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket, int32_t k,
+                              float* out, hipStream_t stream);
+
+hipError_t launch_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n,
+                                  int32_t bucket, int32_t k, float* acc, bool accumulate, hipStream_t stream);
+
 hipError_t launch_majority_vote(const uint32_t* words, int32_t m, int64_t n, int64_t payload_bytes,
                                 uint32_t* out_words, hipStream_t stream);
 

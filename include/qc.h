@@ -378,6 +378,53 @@ int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucke
                        int32_t* isum, int32_t accumulate, float* out, qc_stream_t stream);
 
 /*
+ * Top-k sparsification with error feedback ("Gradient quantization for
+ * communication", section "Quantization Schemes": send only the largest K%
+ * of the gradient; "Gradient Compression and Quantised Collectives", the
+ * opening section -- only the largest-magnitude coordinates -- and section
+ * "Why sparsification fights the all-reduce" -- index-value pairs whose sum
+ * is not closed, so their exchange is an all-gather; section "Error
+ * feedback is the component that makes it work").
+ *
+ * Per bucket (the last may be short, count elements), k_b = min(k, count)
+ * coordinates of largest |v| are sent, v = x + ef; magnitudes compare as
+ * the fp32 bit pattern with the sign cleared, and equal magnitudes go to
+ * the smaller index.  Bucket b's pairs fill slots [b*k, b*k + k_b) of
+ * values (fp32 v) and indices (uint32 index inside the bucket) in ascending
+ * index order; slots [b*k + k_b, (b+1)*k) hold index 0xFFFFFFFF and value
+ * +0.  With ef: ef = v for unsent coordinates and v - v (= +0) for sent ones.
+ *
+ *   bucket  a power of two in [64, QC_MAX_TOPK_BUCKET].  k in [1, bucket].
+ *   values, indices  nb * k entries each, written (4-byte aligned).
+ * Errors: ARG (NULL x/values/indices, n < 0, bad bucket, k outside
+ *         [1, bucket]), UNSUPPORTED (bucket > QC_MAX_TOPK_BUCKET), ALIGN.
+ */
+#define QC_MAX_TOPK_BUCKET 16384
+int qc_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k, float* values,
+                   uint32_t* indices, qc_stream_t stream);
+
+/*
+ * out[i] = 0 for every i < n, then out[b*bucket + idx] = value for each pair
+ * whose idx is below the bucket's count (others, such as 0xFFFFFFFF, are
+ * skipped).  Pairs of one bucket must have distinct indices.
+ * Errors: as qc_encode_topk (out 16-byte aligned).
+ */
+int qc_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket, int32_t k,
+                   float* out, qc_stream_t stream);
+
+/*
+ * The receive-side sum of m workers' top-k payloads stored back to back
+ * (worker w's pairs at w * nb * k): acc = (accumulate ? acc : +0), then for
+ * w = 0..m-1 in order, acc[b*bucket + idx] = acc[b*bucket + idx] + value for
+ * each valid pair.  Elements no pair touches keep their value.  The pairs of
+ * one worker within a bucket must have distinct indices (as the encoder
+ * writes them); repeated indices give an unspecified sum.
+ * Errors: as qc_encode_topk, plus ARG for m outside [1, QC_MAX_WORKERS].
+ */
+int qc_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n, int32_t bucket,
+                       int32_t k, float* acc, int32_t accumulate, qc_stream_t stream);
+
+/*
  * signSGD aggregation by majority vote ("Quantization for Communication",
  * section "Quantized SGD Algorithms", SignSGD; "Gradient Compression and
  * Quantised Collectives", section "Why sparsification fights the

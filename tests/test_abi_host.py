@@ -316,3 +316,30 @@ def test_multi_entry_point_errors(qc):
     args = list(ok)
     args[9] = A + 2
     assert call(qc, f, *args) == qc.QC_ERR_ALIGN
+
+
+def test_topk_errors(qc):
+    f = "qc_encode_topk"
+    ok = (A, A, 1000, 512, 8, A, A, None)
+    for k in (0, -1, 513):
+        assert call(qc, f, A, A, 1000, 512, k, A, A, None) == qc.QC_ERR_ARG, k
+    assert call(qc, f, A, A, 1000, 500, 8, A, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 100000, 32768, 8, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    for pos in (0, 5, 6):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    for pos, bad in ((0, MIS), (1, MIS), (5, A + 2), (6, A + 1)):
+        args = list(ok)
+        args[pos] = bad
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    assert call(qc, f, NULL, NULL, 0, 512, 8, NULL, NULL, None) == qc.QC_OK
+    f = "qc_decode_topk"
+    assert call(qc, f, A, A, 1000, 512, 600, A, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 512, 8, NULL, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 1000, 512, 8, MIS, None) == qc.QC_ERR_ALIGN
+    f = "qc_topk_accumulate"
+    assert call(qc, f, A, A, 0, 1000, 512, 8, A, 0, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 3, 1000, 512, 8, NULL, 0, None) == qc.QC_ERR_ARG
+    assert call(qc, f, A, A, 3, 1000, 512, 8, MIS, 0, None) == qc.QC_ERR_ALIGN
+    assert call(qc, f, NULL, NULL, 3, 0, 512, 8, NULL, 0, None) == qc.QC_OK
