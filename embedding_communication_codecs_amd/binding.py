@@ -23,7 +23,7 @@ QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
 QC_INDEX_SHIFT = 12
 QC_MAX_LIST_BUCKET = 32768
-QC_MAX_TOPK_BUCKET = 16384
+QC_MAX_TOPK_BUCKET = 8192
 
 EXPORTS = (
     "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_uniform_multi", "qc_encode_fp8_rowwise",

@@ -4,13 +4,17 @@
 // Encoder: one block per bucket.  Thread t holds EPT consecutive elements
 // of the bucket in registers (v = ef + x).  The k-th largest magnitude key
 // (the fp32 bits with the sign cleared, which order like |v|) is found
-// exactly by a most-significant-digit radix select: four passes over the
-// 31 key bits (8, 8, 8 and 7 bits), each building an LDS histogram of the
-// next digit among the elements that match the digits fixed so far.  Then
-// every element with a larger key is sent, and of those equal to the
-// threshold the ones with the smallest indices, as many as are still
-// needed.  One block-wide exclusive scan of (larger, equal) counts gives
-// every sent element its slot, so the pairs come out in index order.
+// exactly.  For k up to KSMALL: tau, the k-th largest of the threads'
+// maxima, bounds it from below (k threads hold an element at or above tau),
+// the few elements at or above tau are gathered in LDS and one wave picks
+// the k-th largest among them.  Otherwise, or when too many elements pass
+// tau: a most-significant-digit radix select, four passes over the 31 key
+// bits (8, 8, 8 and 7 bits), each building an LDS histogram of the next
+// digit among the elements that match the digits fixed so far.  Then every
+// element with a larger key is sent, and of those equal to the threshold
+// the ones with the smallest indices, as many as are still needed.  One
+// block-wide exclusive scan of (larger, equal) counts gives every sent
+// element its slot, so the pairs come out in index order.
 //
 // Decoder and sum: one block per bucket; the bucket's span of the dense
 // output is written with zeros (unless the sum continues from the caller's
@@ -24,23 +28,26 @@ namespace qc {
 namespace {
 
 constexpr uint32_t kNoIndex = 0xFFFFFFFFu;
+constexpr int KSMALL = 32;     // k up to this takes the candidate path
+constexpr int CAND_CAP = 256;  // candidates the one-wave selection can hold
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
-// Block-wide exclusive scan of two counters (thread order); `lds` holds
-// 2 * (T/64) values.  Ends with a barrier, so lds can be reused.
+// Block-wide exclusive scan of two counters (thread order), with the block
+// totals; `lds` holds 2 * (T/64) values.  Ends with a barrier, so lds can
+// be reused.
 template <int T>
 __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t& ea, uint32_t& eb,
-                                                      uint32_t* lds) {
+                                                      uint32_t& ta, uint32_t& tb, uint32_t* lds) {
     constexpr int NW = T / WAVE;
     uint32_t ia = a, ib = b;  // inclusive scans inside the wave
 #pragma unroll
     for (int off = 1; off < WAVE; off <<= 1) {
-        const uint32_t ta = (uint32_t)__shfl_up((int)ia, off, WAVE);
-        const uint32_t tb = (uint32_t)__shfl_up((int)ib, off, WAVE);
+        const uint32_t ua = (uint32_t)__shfl_up((int)ia, off, WAVE);
+        const uint32_t ub = (uint32_t)__shfl_up((int)ib, off, WAVE);
         if (lane_id() >= off) {
-            ia += ta;
-            ib += tb;
+            ia += ua;
+            ib += ub;
         }
     }
     if constexpr (NW > 1) {
@@ -49,18 +56,71 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, ui
             lds[NW + wave_id()] = ib;
         }
         __syncthreads();
-        uint32_t pa = 0, pb = 0;
-        for (int w = 0; w < wave_id(); ++w) {
-            pa += lds[w];
-            pb += lds[NW + w];
+        uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
+        for (int w = 0; w < NW; ++w) {
+            if (w < wave_id()) {
+                pa += lds[w];
+                pb += lds[NW + w];
+            }
+            sa += lds[w];
+            sb += lds[NW + w];
         }
         __syncthreads();
         ea = pa + ia - a;
         eb = pb + ib - b;
+        ta = sa;
+        tb = sb;
     } else {
         ea = ia - a;
         eb = ib - b;
+        ta = (uint32_t)__shfl((int)ia, WAVE - 1, WAVE);
+        tb = (uint32_t)__shfl((int)ib, WAVE - 1, WAVE);
     }
+}
+
+// Maximum over the wave, returned wave-uniform; all 64 lanes must be
+// active.  DPP moves combine lanes inside each row of 16 (swap neighbours,
+// swap pairs, mirror each half row, mirror the row), then the four row
+// maxima are read out with v_readlane.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return umax(umax(r0, r1), umax(r2, r3));
+}
+
+// The r-th largest (r = 1..K) of the values held by a wave, Q per lane,
+// counted with multiplicity; values are encoded key+1, 0 meaning "none".
+// Returns 0 if the wave holds fewer than r values.  Destroys c.
+template <int Q>
+__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t (&c)[Q], uint32_t r) {
+    uint32_t m = 0;
+    for (uint32_t it = 0; it < r; ++it) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) best = c[q] > best ? c[q] : best;
+        m = wave_max_u32(best);
+        if (m == 0) break;  // fewer than r values (wave-uniform)
+        // one occurrence is removed: the first lane holding it, its first slot
+        const uint64_t holders = __ballot(best == m);
+        if (lane_id() == __builtin_ctzll(holders)) {
+            bool done = false;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                if (!done && c[q] == m) {
+                    c[q] = 0;
+                    done = true;
+                }
+        }
+    }
+    return m;
 }
 
 template <int T, int EPT, bool EF>
@@ -68,9 +128,12 @@ __global__ void __launch_bounds__(T)
 k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, int32_t k,
            float* __restrict__ values, uint32_t* __restrict__ indices) {
     constexpr int B = T * EPT;
+    constexpr int NW = T / WAVE;
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t bcast[2];
-    __shared__ uint32_t scan_lds[2 * (T / WAVE)];
+    __shared__ uint32_t bcast[4];
+    __shared__ uint32_t scan_lds[2 * NW];
+    __shared__ uint32_t tmax[T];                // each thread's largest key (+1)
+    __shared__ uint32_t cand[CAND_CAP];         // keys (+1) of the elements at or above tau
 
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * B;
@@ -103,47 +166,116 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
         uint32_t thr = 0, need_eq = kb;
         const bool all = kb == (uint32_t)cnt;
         if (!all) {
-            uint32_t prefix = 0, pmask = 0, krem = kb;
-#pragma unroll 1
-            for (int pass = 0; pass < 4; ++pass) {
-                const int shift = pass == 3 ? 0 : 23 - 8 * pass;
-                const uint32_t dmask = pass == 3 ? 0x7Fu : 0xFFu;
-                for (int i = threadIdx.x; i < 256; i += T) hist[i] = 0u;
+            // A lower bound tau on the threshold: the kb-th largest of the
+            // threads' maxima (kb threads each hold an element at or above
+            // it).  Only elements at or above tau can be sent.
+            uint32_t tau1 = 0;  // tau + 1; 0 means no bound
+            if (kb <= (uint32_t)KSMALL) {
+                uint32_t lmax = 0;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e)
+                    if (first + e < cnt) {
+                        const uint32_t k1 = mag_key(v[e]) + 1u;
+                        lmax = k1 > lmax ? k1 : lmax;
+                    }
+                tmax[threadIdx.x] = lmax;
                 __syncthreads();
+                if (threadIdx.x < WAVE) {
+                    constexpr int Q = T / WAVE;
+                    uint32_t c[Q];
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) c[q] = tmax[q * WAVE + lane_id()];
+                    const uint32_t t = wave_rth_largest<Q>(c, kb);
+                    if (lane_id() == 0) bcast[2] = t;
+                }
+                __syncthreads();
+                tau1 = bcast[2];
+            }
+            const uint32_t tau = tau1 == 0 ? 0u : tau1 - 1u;
+
+            // candidates (key >= tau), counted and placed in index order
+            uint32_t nc = 0;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) nc += (first + e < cnt && mag_key(v[e]) >= tau) ? 1u : 0u;
+            uint32_t off, unused, ncand, unused_t;
+            block_exclusive_scan2<T>(nc, 0u, off, unused, ncand, unused_t, scan_lds);
+
+            if (kb <= (uint32_t)KSMALL && ncand <= (uint32_t)CAND_CAP) {
 #pragma unroll
                 for (int e = 0; e < EPT; ++e) {
                     const uint32_t key = mag_key(v[e]);
-                    if (first + e < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+                    if (first + e < cnt && key >= tau) cand[off++] = key + 1u;
                 }
                 __syncthreads();
                 if (threadIdx.x < WAVE) {
-                    // lane l holds bins 4l..4l+3; suffix sums from the top bin down
-                    const int l = lane_id();
-                    const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
-                    uint32_t s = h0 + h1 + h2 + h3;
+                    constexpr int Q = CAND_CAP / WAVE;
+                    uint32_t c[Q], keep[Q];
 #pragma unroll
-                    for (int off = 1; off < WAVE; off <<= 1) {
-                        const uint32_t t = (uint32_t)__shfl_down((int)s, off, WAVE);
-                        if (l + off < WAVE) s += t;
+                    for (int q = 0; q < Q; ++q) {
+                        const uint32_t j = q * WAVE + lane_id();
+                        c[q] = keep[q] = j < ncand ? cand[j] : 0u;
                     }
-                    // s = sum of bins >= 4l; suffix(d) for this lane's bins:
-                    const uint32_t s3 = s - h0 - h1 - h2, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-                    const uint32_t above = s3 - h3;  // sum of bins >= 4l + 4
-                    // the digit d with suffix(d) >= krem > suffix(d + 1)
-                    if (s3 >= krem && above < krem) { bcast[0] = 4 * l + 3; bcast[1] = above; }
-                    if (s2 >= krem && s3 < krem) { bcast[0] = 4 * l + 2; bcast[1] = s3; }
-                    if (s1 >= krem && s2 < krem) { bcast[0] = 4 * l + 1; bcast[1] = s2; }
-                    if (s0 >= krem && s1 < krem) { bcast[0] = 4 * l; bcast[1] = s1; }
+                    const uint32_t t1 = wave_rth_largest<Q>(c, kb);  // the kb-th largest key + 1
+                    uint32_t gt = 0;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) gt += keep[q] > t1 ? 1u : 0u;
+#pragma unroll
+                    for (int off2 = 1; off2 < WAVE; off2 <<= 1) gt += (uint32_t)__shfl_xor((int)gt, off2, WAVE);
+                    if (lane_id() == 0) {
+                        bcast[0] = t1 - 1u;
+                        bcast[1] = kb - gt;
+                    }
                 }
                 __syncthreads();
-                const uint32_t d = bcast[0];
-                krem -= bcast[1];
-                prefix |= d << shift;
-                pmask |= dmask << shift;
-                __syncthreads();  // bcast is rewritten in the next pass
+                thr = bcast[0];
+                need_eq = bcast[1];
+                __syncthreads();  // bcast and cand are rewritten for the next bucket
+            } else {
+                // radix select among the candidates
+                uint32_t prefix = 0, pmask = 0, krem = kb;
+#pragma unroll 1
+                for (int pass = 0; pass < 4; ++pass) {
+                    const int shift = pass == 3 ? 0 : 23 - 8 * pass;
+                    const uint32_t dmask = pass == 3 ? 0x7Fu : 0xFFu;
+                    for (int i = threadIdx.x; i < 256; i += T) hist[i] = 0u;
+                    __syncthreads();
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) {
+                        const uint32_t key = mag_key(v[e]);
+                        if (first + e < cnt && key >= tau && (key & pmask) == prefix)
+                            atomicAdd(&hist[(key >> shift) & dmask], 1u);
+                    }
+                    __syncthreads();
+                    if (threadIdx.x < WAVE) {
+                        // lane l holds bins 4l..4l+3; suffix sums from the top bin down
+                        const int l = lane_id();
+                        const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2],
+                                       h3 = hist[4 * l + 3];
+                        uint32_t su = h0 + h1 + h2 + h3;
+#pragma unroll
+                        for (int o = 1; o < WAVE; o <<= 1) {
+                            const uint32_t t = (uint32_t)__shfl_down((int)su, o, WAVE);
+                            if (l + o < WAVE) su += t;
+                        }
+                        // su = sum of bins >= 4l; suffix(d) for this lane's bins:
+                        const uint32_t s3 = su - h0 - h1 - h2, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+                        const uint32_t above = s3 - h3;  // sum of bins >= 4l + 4
+                        // the digit d with suffix(d) >= krem > suffix(d + 1)
+                        if (s3 >= krem && above < krem) { bcast[0] = 4 * l + 3; bcast[1] = above; }
+                        if (s2 >= krem && s3 < krem) { bcast[0] = 4 * l + 2; bcast[1] = s3; }
+                        if (s1 >= krem && s2 < krem) { bcast[0] = 4 * l + 1; bcast[1] = s2; }
+                        if (s0 >= krem && s1 < krem) { bcast[0] = 4 * l; bcast[1] = s1; }
+                    }
+                    __syncthreads();
+                    const uint32_t d = bcast[0];
+                    krem -= bcast[1];
+                    prefix |= d << shift;
+                    pmask |= dmask << shift;
+                    __syncthreads();  // bcast is rewritten in the next pass
+                }
+                thr = prefix;
+                need_eq = krem;
             }
-            thr = prefix;
-            need_eq = krem;
         }
 
         // counts of larger and equal keys in this thread, scanned over the block
@@ -156,48 +288,54 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
                 eq += (all || key == thr) ? 1u : 0u;
             }
         }
-        uint32_t gt_r, eq_r;
-        block_exclusive_scan2<T>(gt, eq, gt_r, eq_r, scan_lds);
+        uint32_t gt_r, eq_r, gt_all, eq_all;
+        block_exclusive_scan2<T>(gt, eq, gt_r, eq_r, gt_all, eq_all, scan_lds);
 
-        float e_out[EPT];
+        // pairs in index order; the residual written four elements at a time
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const uint32_t key = mag_key(v[e]);
-            bool sel = false;
-            uint32_t pos = 0;
-            if (first + e < cnt) {
-                if (!all && key > thr) {
-                    sel = true;
-                    pos = gt_r + (eq_r < need_eq ? eq_r : need_eq);
-                    ++gt_r;
-                } else if (all || key == thr) {
-                    if (eq_r < need_eq) {
+        for (int q = 0; q < (EPT + 3) / 4; ++q) {
+            float eo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * q + j;
+                if (e >= EPT) break;
+                const uint32_t key = mag_key(v[e]);
+                bool sel = false;
+                uint32_t pos = 0;
+                if (first + e < cnt) {
+                    if (!all && key > thr) {
                         sel = true;
-                        pos = gt_r + eq_r;
+                        pos = gt_r + (eq_r < need_eq ? eq_r : need_eq);
+                        ++gt_r;
+                    } else if (all || key == thr) {
+                        if (eq_r < need_eq) {
+                            sel = true;
+                            pos = gt_r + eq_r;
+                        }
+                        ++eq_r;
                     }
-                    ++eq_r;
+                }
+                if (sel) {
+                    values[bk * k + pos] = v[e];
+                    indices[bk * k + pos] = (uint32_t)(first + e);
+                }
+                eo[j] = sel ? v[e] - v[e] : v[e];
+            }
+            if constexpr (EF) {
+                if (EPT % 4 == 0 && full) {
+                    st_f4(ef + lo + first + 4 * q, f32x4{eo[0], eo[1], eo[2], eo[3]});
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = 4 * q + j;
+                        if (e < EPT && first + e < cnt) ef[lo + first + e] = eo[j];
+                    }
                 }
             }
-            if (sel) {
-                values[bk * k + pos] = v[e];
-                indices[bk * k + pos] = (uint32_t)(first + e);
-            }
-            e_out[e] = sel ? v[e] - v[e] : v[e];
         }
         for (int64_t j = (int64_t)kb + threadIdx.x; j < k; j += T) {
             values[bk * k + j] = 0.0f;
             indices[bk * k + j] = kNoIndex;
-        }
-        if constexpr (EF) {
-            if (full && EPT % 4 == 0) {
-#pragma unroll
-                for (int q = 0; q < EPT / 4; ++q)
-                    st_f4(ef + lo + first + 4 * q, f32x4{e_out[4 * q], e_out[4 * q + 1], e_out[4 * q + 2], e_out[4 * q + 3]});
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPT; ++e)
-                    if (first + e < cnt) ef[lo + first + e] = e_out[e];
-            }
         }
         __syncthreads();  // hist and scan space are reused by the next bucket
     }
@@ -274,7 +412,6 @@ hipError_t launch_encode_topk(const float* x, float* ef, int64_t n, int32_t buck
         case 2048: return launch_enc<128, 16>(x, ef, n, nb, k, values, indices, stream);
         case 4096: return launch_enc<256, 16>(x, ef, n, nb, k, values, indices, stream);
         case 8192: return launch_enc<512, 16>(x, ef, n, nb, k, values, indices, stream);
-        case 16384: return launch_enc<1024, 16>(x, ef, n, nb, k, values, indices, stream);
         default: return hipErrorInvalidValue;
     }
 }

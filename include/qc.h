@@ -399,7 +399,7 @@ int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucke
  * Errors: ARG (NULL x/values/indices, n < 0, bad bucket, k outside
  *         [1, bucket]), UNSUPPORTED (bucket > QC_MAX_TOPK_BUCKET), ALIGN.
  */
-#define QC_MAX_TOPK_BUCKET 16384
+#define QC_MAX_TOPK_BUCKET 8192
 int qc_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k, float* values,
                    uint32_t* indices, qc_stream_t stream);
 

@@ -324,7 +324,7 @@ def test_topk_errors(qc):
     for k in (0, -1, 513):
         assert call(qc, f, A, A, 1000, 512, k, A, A, None) == qc.QC_ERR_ARG, k
     assert call(qc, f, A, A, 1000, 500, 8, A, A, None) == qc.QC_ERR_ARG
-    assert call(qc, f, A, A, 100000, 32768, 8, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, A, A, 100000, 16384, 8, A, A, None) == qc.QC_ERR_UNSUPPORTED
     for pos in (0, 5, 6):
         args = list(ok)
         args[pos] = NULL
