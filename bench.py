@@ -79,9 +79,25 @@ def tensor_list_sizes():
     return layer * T_L
 
 
-def source_hash() -> str:
+# The kernel source each op runs (plus the shared headers below): counter
+# traffic taken for an op stays valid while these files are unchanged.
+SHARED_SOURCES = ["qc_device.hpp", "qc_bucket.hpp", "qc_launch.hpp", "../../include/qc.h"]
+OP_SOURCE = {
+    **{o: "k_encode.hip" for o in ("uniform_enc", "qsgd_enc", "sign_enc", "int2_enc", "stoch4_enc", "tern_enc",
+                                   "shared_absmax", "shared_enc", "list_enc", "list_enc_per_tensor")},
+    "fp8_enc": "k_fp8.hip",
+    **{o: "k_decode.hip" for o in ("uniform_dec", "fp8_dec", "qsgd_dec", "sign_dec", "int2_dec", "tern_dec",
+                                   "list_dec")},
+    **{o: "k_accumulate.hip" for o in ("acc_requant", "acc_tern", "acc_int2_requant")},
+    "sign_vote": "k_vote.hip",
+    "shared_sum": "k_shared_sum.hip",
+    **{o: "k_topk.hip" for o in ("topk_enc", "topk_dec", "topk_sum")},
+}
+
+
+def source_hash(op: str) -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in [OP_SOURCE[op]] + SHARED_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -484,16 +500,16 @@ def calibrate(torch, reps=10):
 
 def load_traffic(kernel_op):
     """HBM bytes per launch measured with rocprofv3 counters for this op,
-    if they were taken on the current kernel sources."""
+    if they were taken on the op's current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash():
-        return None
     e = t.get("ops", {}).get(kernel_op)
-    return None if e is None else e.get("hbm_bytes")
+    if e is None or e.get("source_hash") != source_hash(kernel_op):
+        return None
+    return e.get("hbm_bytes")
 
 
 def time_ops(torch, ops, names, sizes, steps, warmup, extra):
