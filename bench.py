@@ -22,7 +22,7 @@ pass) and shared-scale INT8 (an exact integer sum, dequantized once); and
 the bucketing front-end on the parameter list of a 24-layer, width-1024
 transformer (288 tensors, 302M fp32): INT8 + EF of the whole list in one
 launch, the same tensors encoded one launch per tensor, and the decode back
-into the list; top-k sparsification (8 of every 8,192 coordinates, error
+into the list; top-k sparsification (4 of every 4,096 coordinates, error
 feedback) of the 1e9 gradient, its decode, and the sum of 64 workers'
 top-k payloads of 2^26.  They are reported
 under `extensions`, in the same form as `ops`.
@@ -69,8 +69,8 @@ X_M, X_AN, X_AB = 64, 1 << 26, 2048
 # width 1024 (per layer: qkv weight and bias, output projection weight and
 # bias, two layer norms' weight and bias, two MLP weights and biases)
 T_D, T_L, T_B = 1024, 24, 4096
-# top-k: density about 1/1000 (8 of every 8,192 coordinates)
-K_B, K_K = 8192, 8
+# top-k: density about 1/1000 (4 of every 4,096 coordinates)
+K_B, K_K = 4096, 4
 
 
 def tensor_list_sizes():

@@ -28,8 +28,7 @@ namespace qc {
 namespace {
 
 constexpr uint32_t kNoIndex = 0xFFFFFFFFu;
-constexpr int KSMALL = 32;     // k up to this takes the candidate path
-constexpr int CAND_CAP = 256;  // candidates the one-wave selection can hold
+constexpr int KSMALL = 16;  // k up to this takes the candidate path
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
@@ -123,17 +122,33 @@ __device__ __forceinline__ uint32_t wave_rth_largest(uint32_t (&c)[Q], uint32_t 
     return m;
 }
 
+// Exclusive scan over the wave (lane order) and the wave total.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t a, uint32_t& total) {
+    uint32_t i = a;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)i, off, WAVE);
+        if (lane_id() >= off) i += t;
+    }
+    total = (uint32_t)__shfl((int)i, WAVE - 1, WAVE);
+    return i - a;
+}
+
 template <int T, int EPT, bool EF>
 __global__ void __launch_bounds__(T)
 k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64_t nb, int32_t k,
            float* __restrict__ values, uint32_t* __restrict__ indices) {
     constexpr int B = T * EPT;
     constexpr int NW = T / WAVE;
+    constexpr int CAPW = 32;               // candidates one wave may hand over
+    constexpr int QC = (NW * CAPW + WAVE - 1) / WAVE;  // candidates per lane of wave 0
     __shared__ uint32_t hist[256];
     __shared__ uint32_t bcast[4];
     __shared__ uint32_t scan_lds[2 * NW];
-    __shared__ uint32_t tmax[T];                // each thread's largest key (+1)
-    __shared__ uint32_t cand[CAND_CAP];         // keys (+1) of the elements at or above tau
+    __shared__ uint32_t cbits[NW * CAPW];  // candidates of wave w at [w*CAPW, ...): fp32 bits,
+    __shared__ uint32_t cidx[NW * CAPW];   // index in the bucket,
+    __shared__ uint32_t csel[NW * CAPW];   // and whether it is sent
+    __shared__ uint32_t wcount[NW];
 
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * B;
@@ -142,12 +157,14 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
         const uint32_t kb = (uint32_t)((int64_t)k < cnt ? k : cnt);
         const int32_t first = threadIdx.x * EPT;  // local index of this thread's element 0
 
+        // a thread's EPT elements are 4*EPT contiguous bytes; plain loads and
+        // stores let L2 merge the lanes' pieces into whole lines
         float v[EPT];
         if (full && EPT % 4 == 0) {
 #pragma unroll
             for (int q = 0; q < EPT / 4; ++q) {
-                f32x4 g = ld_stream_f4(x + lo + first + 4 * q);
-                if constexpr (EF) g = ld_stream_f4(ef + lo + first + 4 * q) + g;
+                f32x4 g = ld_f4(x + lo + first + 4 * q);
+                if constexpr (EF) g = ld_f4(ef + lo + first + 4 * q) + g;
                 v[4 * q] = g.x; v[4 * q + 1] = g.y; v[4 * q + 2] = g.z; v[4 * q + 3] = g.w;
             }
         } else {
@@ -162,76 +179,141 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
             }
         }
 
-        // threshold key and how many elements equal to it are still needed
-        uint32_t thr = 0, need_eq = kb;
         const bool all = kb == (uint32_t)cnt;
-        if (!all) {
-            // A lower bound tau on the threshold: the kb-th largest of the
-            // threads' maxima (kb threads each hold an element at or above
-            // it).  Only elements at or above tau can be sent.
-            uint32_t tau1 = 0;  // tau + 1; 0 means no bound
-            if (kb <= (uint32_t)KSMALL) {
-                uint32_t lmax = 0;
+        bool fast = !all && kb <= (uint32_t)KSMALL;  // block-uniform
+        uint32_t my_off = 0, tw = 0;                 // this thread's first candidate slot; its wave's bound
+        if (fast) {
+            // The wave's bound tw: the kb-th largest of its threads' maxima.
+            // kb elements of the bucket are at or above it, so the bucket's
+            // threshold is too, and elements below tw are never sent.
+            uint32_t lmax = 0;
 #pragma unroll
-                for (int e = 0; e < EPT; ++e)
-                    if (first + e < cnt) {
-                        const uint32_t k1 = mag_key(v[e]) + 1u;
-                        lmax = k1 > lmax ? k1 : lmax;
-                    }
-                tmax[threadIdx.x] = lmax;
-                __syncthreads();
-                if (threadIdx.x < WAVE) {
-                    constexpr int Q = T / WAVE;
-                    uint32_t c[Q];
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) c[q] = tmax[q * WAVE + lane_id()];
-                    const uint32_t t = wave_rth_largest<Q>(c, kb);
-                    if (lane_id() == 0) bcast[2] = t;
+            for (int e = 0; e < EPT; ++e)
+                if (first + e < cnt) {
+                    const uint32_t k1 = mag_key(v[e]) + 1u;
+                    lmax = k1 > lmax ? k1 : lmax;
                 }
-                __syncthreads();
-                tau1 = bcast[2];
-            }
-            const uint32_t tau = tau1 == 0 ? 0u : tau1 - 1u;
-
-            // candidates (key >= tau), counted and placed in index order
+            uint32_t c1[1] = {lmax};
+            const uint32_t tw1 = wave_rth_largest<1>(c1, kb);
+            tw = tw1 == 0 ? 0u : tw1 - 1u;
             uint32_t nc = 0;
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) nc += (first + e < cnt && mag_key(v[e]) >= tau) ? 1u : 0u;
-            uint32_t off, unused, ncand, unused_t;
-            block_exclusive_scan2<T>(nc, 0u, off, unused, ncand, unused_t, scan_lds);
+            for (int e = 0; e < EPT; ++e) nc += (first + e < cnt && mag_key(v[e]) >= tw) ? 1u : 0u;
+            uint32_t wtotal;
+            my_off = wave_excl_scan(nc, wtotal);
+            if (wtotal <= (uint32_t)CAPW) {
+                uint32_t o = wave_id() * CAPW + my_off;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e)
+                    if (first + e < cnt && mag_key(v[e]) >= tw) {
+                        cbits[o] = __float_as_uint(v[e]);
+                        cidx[o] = (uint32_t)(first + e);
+                        ++o;
+                    }
+            }
+            if (lane_id() == 0) wcount[wave_id()] = wtotal;
+            __syncthreads();
+            uint32_t total = 0;
+            bool over = false;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                over = over || wcount[w] > (uint32_t)CAPW;
+                total += wcount[w];
+            }
+            fast = !over;
+            if (fast && threadIdx.x < WAVE) {
+                // wave 0: lane l takes candidates [l*QC, (l+1)*QC) of the
+                // waves' lists one after the other, which is index order
+                uint32_t pw[NW];
+                uint32_t acc = 0;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    pw[w] = acc;
+                    acc += wcount[w];
+                }
+                uint32_t key1[QC], work[QC], slot[QC];
+#pragma unroll
+                for (int q = 0; q < QC; ++q) {
+                    const uint32_t j = lane_id() * QC + q;
+                    uint32_t sl = 0, kv = 0;
+                    if (j < total) {
+#pragma unroll
+                        for (int w = 0; w < NW; ++w)
+                            if (j >= pw[w] && j < pw[w] + wcount[w]) sl = w * CAPW + (j - pw[w]);
+                        kv = (cbits[sl] & 0x7FFFFFFFu) + 1u;
+                    }
+                    key1[q] = work[q] = kv;
+                    slot[q] = sl;
+                }
+                const uint32_t t1 = wave_rth_largest<QC>(work, kb);  // threshold key + 1
+                uint32_t gt = 0, eq = 0;
+#pragma unroll
+                for (int q = 0; q < QC; ++q) {
+                    gt += key1[q] > t1 ? 1u : 0u;
+                    eq += key1[q] == t1 ? 1u : 0u;
+                }
+                uint32_t gt_all, eq_all;
+                (void)wave_excl_scan(gt, gt_all);
+                uint32_t eq_r = wave_excl_scan(eq, eq_all);
+                const uint32_t need = kb - gt_all;
+                bool sel[QC];
+                uint32_t ns = 0;
+#pragma unroll
+                for (int q = 0; q < QC; ++q) {
+                    sel[q] = key1[q] > t1;
+                    if (key1[q] == t1) {
+                        sel[q] = eq_r < need;
+                        ++eq_r;
+                    }
+                    ns += sel[q] ? 1u : 0u;
+                }
+                uint32_t ns_all;
+                uint32_t pos = wave_excl_scan(ns, ns_all);
+#pragma unroll
+                for (int q = 0; q < QC; ++q) {
+                    const uint32_t j = lane_id() * QC + q;
+                    if (j < total) csel[slot[q]] = sel[q] ? 1u : 0u;
+                    if (sel[q]) {
+                        values[bk * k + pos] = __uint_as_float(cbits[slot[q]]);
+                        indices[bk * k + pos] = cidx[slot[q]];
+                        ++pos;
+                    }
+                }
+            }
+            if (fast) __syncthreads();  // csel is visible to every thread
+        }
 
-            if (kb <= (uint32_t)KSMALL && ncand <= (uint32_t)CAND_CAP) {
+        if (fast) {
+            // the residual: sent candidates leave v - v, the rest v
+            uint32_t o = wave_id() * CAPW + my_off;
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const uint32_t key = mag_key(v[e]);
-                    if (first + e < cnt && key >= tau) cand[off++] = key + 1u;
+            for (int q = 0; q < (EPT + 3) / 4; ++q) {
+                float eo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * q + j;
+                    if (e >= EPT) break;
+                    bool s = false;
+                    if (first + e < cnt && mag_key(v[e]) >= tw) s = csel[o++] != 0u;
+                    eo[j] = s ? v[e] - v[e] : v[e];
                 }
-                __syncthreads();
-                if (threadIdx.x < WAVE) {
-                    constexpr int Q = CAND_CAP / WAVE;
-                    uint32_t c[Q], keep[Q];
+                if constexpr (EF) {
+                    if (EPT % 4 == 0 && full) {
+                        *reinterpret_cast<f32x4*>(ef + lo + first + 4 * q) = f32x4{eo[0], eo[1], eo[2], eo[3]};
+                    } else {
 #pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        const uint32_t j = q * WAVE + lane_id();
-                        c[q] = keep[q] = j < ncand ? cand[j] : 0u;
-                    }
-                    const uint32_t t1 = wave_rth_largest<Q>(c, kb);  // the kb-th largest key + 1
-                    uint32_t gt = 0;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) gt += keep[q] > t1 ? 1u : 0u;
-#pragma unroll
-                    for (int off2 = 1; off2 < WAVE; off2 <<= 1) gt += (uint32_t)__shfl_xor((int)gt, off2, WAVE);
-                    if (lane_id() == 0) {
-                        bcast[0] = t1 - 1u;
-                        bcast[1] = kb - gt;
+                        for (int j = 0; j < 4; ++j) {
+                            const int e = 4 * q + j;
+                            if (e < EPT && first + e < cnt) ef[lo + first + e] = eo[j];
+                        }
                     }
                 }
-                __syncthreads();
-                thr = bcast[0];
-                need_eq = bcast[1];
-                __syncthreads();  // bcast and cand are rewritten for the next bucket
-            } else {
-                // radix select among the candidates
+            }
+        } else {
+            // threshold key and how many elements equal to it are still needed
+            uint32_t thr = 0, need_eq = kb;
+            if (!all) {
+                // radix select, most significant digit first
                 uint32_t prefix = 0, pmask = 0, krem = kb;
 #pragma unroll 1
                 for (int pass = 0; pass < 4; ++pass) {
@@ -242,8 +324,7 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
 #pragma unroll
                     for (int e = 0; e < EPT; ++e) {
                         const uint32_t key = mag_key(v[e]);
-                        if (first + e < cnt && key >= tau && (key & pmask) == prefix)
-                            atomicAdd(&hist[(key >> shift) & dmask], 1u);
+                        if (first + e < cnt && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
                     }
                     __syncthreads();
                     if (threadIdx.x < WAVE) {
@@ -276,59 +357,59 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
                 thr = prefix;
                 need_eq = krem;
             }
-        }
 
-        // counts of larger and equal keys in this thread, scanned over the block
-        uint32_t gt = 0, eq = 0;
+            // counts of larger and equal keys in this thread, scanned over the block
+            uint32_t gt = 0, eq = 0;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const uint32_t key = mag_key(v[e]);
-            if (first + e < cnt) {
-                gt += (!all && key > thr) ? 1u : 0u;
-                eq += (all || key == thr) ? 1u : 0u;
-            }
-        }
-        uint32_t gt_r, eq_r, gt_all, eq_all;
-        block_exclusive_scan2<T>(gt, eq, gt_r, eq_r, gt_all, eq_all, scan_lds);
-
-        // pairs in index order; the residual written four elements at a time
-#pragma unroll
-        for (int q = 0; q < (EPT + 3) / 4; ++q) {
-            float eo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = 4 * q + j;
-                if (e >= EPT) break;
+            for (int e = 0; e < EPT; ++e) {
                 const uint32_t key = mag_key(v[e]);
-                bool sel = false;
-                uint32_t pos = 0;
                 if (first + e < cnt) {
-                    if (!all && key > thr) {
-                        sel = true;
-                        pos = gt_r + (eq_r < need_eq ? eq_r : need_eq);
-                        ++gt_r;
-                    } else if (all || key == thr) {
-                        if (eq_r < need_eq) {
-                            sel = true;
-                            pos = gt_r + eq_r;
-                        }
-                        ++eq_r;
-                    }
+                    gt += (!all && key > thr) ? 1u : 0u;
+                    eq += (all || key == thr) ? 1u : 0u;
                 }
-                if (sel) {
-                    values[bk * k + pos] = v[e];
-                    indices[bk * k + pos] = (uint32_t)(first + e);
-                }
-                eo[j] = sel ? v[e] - v[e] : v[e];
             }
-            if constexpr (EF) {
-                if (EPT % 4 == 0 && full) {
-                    st_f4(ef + lo + first + 4 * q, f32x4{eo[0], eo[1], eo[2], eo[3]});
-                } else {
+            uint32_t gt_r, eq_r, gt_all, eq_all;
+            block_exclusive_scan2<T>(gt, eq, gt_r, eq_r, gt_all, eq_all, scan_lds);
+
+            // pairs in index order; the residual written four elements at a time
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int e = 4 * q + j;
-                        if (e < EPT && first + e < cnt) ef[lo + first + e] = eo[j];
+            for (int q = 0; q < (EPT + 3) / 4; ++q) {
+                float eo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * q + j;
+                    if (e >= EPT) break;
+                    const uint32_t key = mag_key(v[e]);
+                    bool sel = false;
+                    uint32_t pos = 0;
+                    if (first + e < cnt) {
+                        if (!all && key > thr) {
+                            sel = true;
+                            pos = gt_r + (eq_r < need_eq ? eq_r : need_eq);
+                            ++gt_r;
+                        } else if (all || key == thr) {
+                            if (eq_r < need_eq) {
+                                sel = true;
+                                pos = gt_r + eq_r;
+                            }
+                            ++eq_r;
+                        }
+                    }
+                    if (sel) {
+                        values[bk * k + pos] = v[e];
+                        indices[bk * k + pos] = (uint32_t)(first + e);
+                    }
+                    eo[j] = sel ? v[e] - v[e] : v[e];
+                }
+                if constexpr (EF) {
+                    if (EPT % 4 == 0 && full) {
+                        *reinterpret_cast<f32x4*>(ef + lo + first + 4 * q) = f32x4{eo[0], eo[1], eo[2], eo[3]};
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int e = 4 * q + j;
+                            if (e < EPT && first + e < cnt) ef[lo + first + e] = eo[j];
+                        }
                     }
                 }
             }
@@ -337,7 +418,7 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
             values[bk * k + j] = 0.0f;
             indices[bk * k + j] = kNoIndex;
         }
-        __syncthreads();  // hist and scan space are reused by the next bucket
+        __syncthreads();  // LDS is reused by the next bucket
     }
 }
 
