@@ -157,9 +157,8 @@ def topk_bytes():
         "topk_enc": (4 * X_N, 12 * X_N + pairs),
         # pairs read, the dense vector written (zeros and values)
         "topk_dec": (4 * X_N, pairs + 4 * X_N),
-        # 64 workers' pairs read; the accumulator zeroed, then read and
-        # written where pairs land
-        "topk_sum": (4 * X_M * X_AN, X_M * pairs_w + 4 * X_AN + X_M * pairs_w),
+        # 64 workers' pairs read, the dense sum written once
+        "topk_sum": (4 * X_M * X_AN, X_M * pairs_w + 4 * X_AN),
     }
 
 

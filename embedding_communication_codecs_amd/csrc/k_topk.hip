@@ -16,10 +16,9 @@
 // block-wide exclusive scan of (larger, equal) counts gives every sent
 // element its slot, so the pairs come out in index order.
 //
-// Decoder and sum: one block per bucket; the bucket's span of the dense
-// output is written with zeros (unless the sum continues from the caller's
-// values), then the pairs are placed; a barrier separates workers so the
-// additions happen in worker order.
+// Decoder and sum: one block per bucket, holding the bucket's span of the
+// dense output in LDS (zeros, or the caller's values for a continued sum)
+// while the pairs are placed or added, then writing it out in one pass.
 #include "qc_device.hpp"
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
@@ -422,49 +421,98 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
     }
 }
 
-constexpr int TD = 256;  // threads of the decode and sum kernels
+constexpr int TD = 256;      // threads of the decode and sum kernels
+constexpr int PAIR_CAP = 2048;  // pairs staged in LDS at a time by the sum
 
-// Zeros over [lo, lo + cnt) of a 16-byte aligned bucket span.
-__device__ __forceinline__ void zero_span(float* __restrict__ out, int64_t lo, int64_t cnt) {
-    const int64_t q4 = cnt >> 2;
-    for (int64_t q = threadIdx.x; q < q4; q += TD) st_f4(out + lo + 4 * q, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-    for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += TD) out[lo + i] = 0.0f;
+// The bucket's span [lo, lo + cnt) of a dense vector, from/to an LDS slice.
+__device__ __forceinline__ void slice_load(const float* __restrict__ src, int64_t lo, int64_t cnt, float* slice) {
+    for (int64_t i = threadIdx.x; i < cnt; i += TD) slice[i] = src[lo + i];
+}
+__device__ __forceinline__ void slice_zero(int64_t cnt, float* slice) {
+    for (int64_t i = threadIdx.x; i < cnt; i += TD) slice[i] = 0.0f;
+}
+__device__ __forceinline__ void slice_store(float* __restrict__ dst, int64_t lo, int64_t cnt, const float* slice) {
+    const int64_t q4 = cnt >> 2;  // dst + lo is 16-byte aligned (buckets are multiples of 64)
+    for (int64_t q = threadIdx.x; q < q4; q += TD)
+        *reinterpret_cast<f32x4*>(dst + lo + 4 * q) =
+            f32x4{slice[4 * q], slice[4 * q + 1], slice[4 * q + 2], slice[4 * q + 3]};
+    for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += TD) dst[lo + i] = slice[i];
 }
 
+// Decode: the pairs are placed into a zeroed LDS slice of the bucket, which
+// then goes out with one coalesced pass.
 __global__ void __launch_bounds__(TD)
 k_decode_topk(const float* __restrict__ values, const uint32_t* __restrict__ indices, int64_t n, int64_t nb,
               int32_t bucket, int32_t k, float* __restrict__ out) {
+    extern __shared__ float slice[];
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * bucket;
         const int64_t cnt = n - lo < bucket ? n - lo : bucket;
-        zero_span(out, lo, cnt);
-        __syncthreads();  // the zeros are in memory before any value lands
+        slice_zero(cnt, slice);
+        __syncthreads();
         for (int64_t j = threadIdx.x; j < k; j += TD) {
             const uint32_t idx = indices[bk * k + j];
-            if ((int64_t)idx < cnt) out[lo + idx] = values[bk * k + j];
+            if ((int64_t)idx < cnt) slice[idx] = values[bk * k + j];
         }
+        __syncthreads();
+        slice_store(out, lo, cnt, slice);
         __syncthreads();
     }
 }
 
+// The sum: the bucket's accumulator span lives in LDS while the workers'
+// pairs are added in worker order.  With k < 64 one wave applies them
+// (a worker's pairs have distinct indices, one lane each; a wave's LDS
+// accesses happen in program order, so worker w + 1 sees worker w's sums);
+// larger k uses every thread per worker with a barrier between workers.
 // Pairs of one worker within a bucket must have distinct indices (as the
-// encoder writes them): within a worker the additions run in parallel.
+// encoder writes them).
 __global__ void __launch_bounds__(TD)
 k_topk_accumulate(const float* __restrict__ values, const uint32_t* __restrict__ indices, int32_t m, int64_t n,
                   int64_t nb, int32_t bucket, int32_t k, float* __restrict__ acc, int32_t accumulate) {
+    extern __shared__ float lds[];
+    float* slice = lds;
+    float* pval = lds + bucket;
+    uint32_t* pidx = reinterpret_cast<uint32_t*>(pval + PAIR_CAP);
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * bucket;
         const int64_t cnt = n - lo < bucket ? n - lo : bucket;
-        if (!accumulate) zero_span(acc, lo, cnt);
-        __syncthreads();
-        for (int32_t w = 0; w < m; ++w) {
-            const int64_t base = ((int64_t)w * nb + bk) * k;
-            for (int64_t j = threadIdx.x; j < k; j += TD) {
-                const uint32_t idx = indices[base + j];
-                if ((int64_t)idx < cnt) acc[lo + idx] = acc[lo + idx] + values[base + j];
+        if (accumulate) slice_load(acc, lo, cnt, slice);
+        else slice_zero(cnt, slice);
+        if (k < WAVE) {
+            const int32_t per = PAIR_CAP / k;  // workers per staged chunk
+            for (int32_t w0 = 0; w0 < m; w0 += per) {
+                const int32_t w1 = m - w0 < per ? m : w0 + per;
+                const int32_t np = (w1 - w0) * k;
+                for (int32_t j = threadIdx.x; j < np; j += TD) {
+                    const int64_t src = ((int64_t)(w0 + j / k) * nb + bk) * k + j % k;
+                    pval[j] = values[src];
+                    pidx[j] = indices[src];
+                }
+                __syncthreads();
+                if (threadIdx.x < WAVE) {
+                    for (int32_t w = 0; w < w1 - w0; ++w) {
+                        if (lane_id() < k) {
+                            const uint32_t idx = pidx[w * k + lane_id()];
+                            if ((int64_t)idx < cnt) slice[idx] = slice[idx] + pval[w * k + lane_id()];
+                        }
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();  // worker w's additions land before worker w + 1's
+        } else {
+            __syncthreads();
+            for (int32_t w = 0; w < m; ++w) {
+                const int64_t base = ((int64_t)w * nb + bk) * k;
+                for (int64_t j = threadIdx.x; j < k; j += TD) {
+                    const uint32_t idx = indices[base + j];
+                    if ((int64_t)idx < cnt) slice[idx] = slice[idx] + values[base + j];
+                }
+                __syncthreads();  // worker w's additions land before worker w + 1's
+            }
         }
+        slice_store(acc, lo, cnt, slice);
+        __syncthreads();
     }
 }
 
@@ -500,7 +548,8 @@ hipError_t launch_encode_topk(const float* x, float* ef, int64_t n, int32_t buck
 hipError_t launch_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket, int32_t k,
                               float* out, hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
-    hipLaunchKernelGGL(k_decode_topk, dim3((unsigned)grid_for(nb, 1)), dim3(TD), 0, stream, values, indices, n, nb,
+    const size_t lds = (size_t)bucket * sizeof(float);
+    hipLaunchKernelGGL(k_decode_topk, dim3((unsigned)grid_for(nb, 1)), dim3(TD), lds, stream, values, indices, n, nb,
                        bucket, k, out);
     return hipGetLastError();
 }
@@ -508,7 +557,8 @@ hipError_t launch_decode_topk(const float* values, const uint32_t* indices, int6
 hipError_t launch_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n,
                                   int32_t bucket, int32_t k, float* acc, bool accumulate, hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
-    hipLaunchKernelGGL(k_topk_accumulate, dim3((unsigned)grid_for(nb, 1)), dim3(TD), 0, stream, values, indices, m,
+    const size_t lds = (size_t)bucket * sizeof(float) + (size_t)PAIR_CAP * (sizeof(float) + sizeof(uint32_t));
+    hipLaunchKernelGGL(k_topk_accumulate, dim3((unsigned)grid_for(nb, 1)), dim3(TD), lds, stream, values, indices, m,
                        n, nb, bucket, k, acc, accumulate ? 1 : 0);
     return hipGetLastError();
 }
