@@ -16,12 +16,17 @@
 // block-wide exclusive scan of (larger, equal) counts gives every sent
 // element its slot, so the pairs come out in index order.
 //
-// Decoder and sum: one block per bucket, holding the bucket's span of the
-// dense output in LDS (zeros, or the caller's values for a continued sum)
-// while the pairs are placed or added, then writing it out in one pass.
+// Decoder and sum: the bucket's span of the dense output is held in LDS
+// (zeros, or the caller's values for a continued sum) while the pairs are
+// placed or added, then written out in one pass.  The decoder and the sum
+// for k >= 64 give each bucket a block; the sum for smaller k gives it one
+// wave, which orders the workers' additions to one index without barriers
+// (owner tags in LDS, then worker by worker for whatever is left).
 #include "qc_device.hpp"
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
+
+#include <atomic>
 
 namespace qc {
 namespace {
@@ -421,22 +426,40 @@ k_enc_topk(const float* __restrict__ x, float* __restrict__ ef, int64_t n, int64
     }
 }
 
-constexpr int TD = 256;      // threads of the decode and sum kernels
-constexpr int PAIR_CAP = 2048;  // pairs staged in LDS at a time by the sum
+constexpr int TD = 256;  // threads of the decode kernel and of the sum for k >= 64
 
-// The bucket's span [lo, lo + cnt) of a dense vector, from/to an LDS slice.
-__device__ __forceinline__ void slice_load(const float* __restrict__ src, int64_t lo, int64_t cnt, float* slice) {
-    for (int64_t i = threadIdx.x; i < cnt; i += TD) slice[i] = src[lo + i];
+// The bucket's span [lo, lo + cnt) of a dense vector, from/to the block's
+// 16-byte aligned LDS slice (zeros, or the caller's values), by the NT
+// threads of the block, 16 bytes at a time; dst + lo and src + lo are
+// 16-byte aligned (buckets are multiples of 64).
+template <int NT>
+__device__ __forceinline__ void slice_init(const float* __restrict__ src, int64_t lo, int64_t cnt, float* slice,
+                                           bool load) {
+    const int64_t q4 = cnt >> 2;
+    f32x4* s4 = reinterpret_cast<f32x4*>(slice);
+    if (load) {
+        int64_t q = threadIdx.x;
+        for (; q + 3 * NT < q4; q += 4 * NT) {  // four loads in flight
+            const f32x4 a = ld_f4(src + lo + 4 * q), b = ld_f4(src + lo + 4 * (q + NT)),
+                        c = ld_f4(src + lo + 4 * (q + 2 * NT)), d = ld_f4(src + lo + 4 * (q + 3 * NT));
+            s4[q] = a;
+            s4[q + NT] = b;
+            s4[q + 2 * NT] = c;
+            s4[q + 3 * NT] = d;
+        }
+        for (; q < q4; q += NT) s4[q] = ld_f4(src + lo + 4 * q);
+        for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += NT) slice[i] = src[lo + i];
+    } else {
+        for (int64_t q = threadIdx.x; q < q4; q += NT) s4[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += NT) slice[i] = 0.0f;
+    }
 }
-__device__ __forceinline__ void slice_zero(int64_t cnt, float* slice) {
-    for (int64_t i = threadIdx.x; i < cnt; i += TD) slice[i] = 0.0f;
-}
+template <int NT>
 __device__ __forceinline__ void slice_store(float* __restrict__ dst, int64_t lo, int64_t cnt, const float* slice) {
-    const int64_t q4 = cnt >> 2;  // dst + lo is 16-byte aligned (buckets are multiples of 64)
-    for (int64_t q = threadIdx.x; q < q4; q += TD)
-        *reinterpret_cast<f32x4*>(dst + lo + 4 * q) =
-            f32x4{slice[4 * q], slice[4 * q + 1], slice[4 * q + 2], slice[4 * q + 3]};
-    for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += TD) dst[lo + i] = slice[i];
+    const int64_t q4 = cnt >> 2;
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(slice);
+    for (int64_t q = threadIdx.x; q < q4; q += NT) *reinterpret_cast<f32x4*>(dst + lo + 4 * q) = s4[q];
+    for (int64_t i = 4 * q4 + threadIdx.x; i < cnt; i += NT) dst[lo + i] = slice[i];
 }
 
 // Decode: the pairs are placed into a zeroed LDS slice of the bucket, which
@@ -444,76 +467,254 @@ __device__ __forceinline__ void slice_store(float* __restrict__ dst, int64_t lo,
 __global__ void __launch_bounds__(TD)
 k_decode_topk(const float* __restrict__ values, const uint32_t* __restrict__ indices, int64_t n, int64_t nb,
               int32_t bucket, int32_t k, float* __restrict__ out) {
-    extern __shared__ float slice[];
+    extern __shared__ f32x4 lds4[];
+    float* slice = reinterpret_cast<float*>(lds4);
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * bucket;
         const int64_t cnt = n - lo < bucket ? n - lo : bucket;
-        slice_zero(cnt, slice);
+        slice_init<TD>(nullptr, lo, cnt, slice, false);
         __syncthreads();
         for (int64_t j = threadIdx.x; j < k; j += TD) {
             const uint32_t idx = indices[bk * k + j];
             if ((int64_t)idx < cnt) slice[idx] = values[bk * k + j];
         }
         __syncthreads();
-        slice_store(out, lo, cnt, slice);
+        slice_store<TD>(out, lo, cnt, slice);
         __syncthreads();
     }
 }
 
-// The sum: the bucket's accumulator span lives in LDS while the workers'
-// pairs are added in worker order.  With k < 64 one wave applies them
-// (a worker's pairs have distinct indices, one lane each; a wave's LDS
-// accesses happen in program order, so worker w + 1 sees worker w's sums);
-// larger k uses every thread per worker with a barrier between workers.
-// Pairs of one worker within a bucket must have distinct indices (as the
-// encoder writes them).
+// The sum for k >= 64: the bucket's accumulator span lives in LDS; every
+// thread adds pairs of worker w, with a barrier between workers.  Pairs of
+// one worker within a bucket must have distinct indices (as the encoder
+// writes them).
 __global__ void __launch_bounds__(TD)
 k_topk_accumulate(const float* __restrict__ values, const uint32_t* __restrict__ indices, int32_t m, int64_t n,
                   int64_t nb, int32_t bucket, int32_t k, float* __restrict__ acc, int32_t accumulate) {
-    extern __shared__ float lds[];
-    float* slice = lds;
-    float* pval = lds + bucket;
-    uint32_t* pidx = reinterpret_cast<uint32_t*>(pval + PAIR_CAP);
+    extern __shared__ f32x4 lds4[];
+    float* slice = reinterpret_cast<float*>(lds4);
     for (int64_t bk = blockIdx.x; bk < nb; bk += gridDim.x) {
         const int64_t lo = bk * bucket;
         const int64_t cnt = n - lo < bucket ? n - lo : bucket;
-        if (accumulate) slice_load(acc, lo, cnt, slice);
-        else slice_zero(cnt, slice);
-        if (k < WAVE) {
-            const int32_t per = PAIR_CAP / k;  // workers per staged chunk
-            for (int32_t w0 = 0; w0 < m; w0 += per) {
-                const int32_t w1 = m - w0 < per ? m : w0 + per;
-                const int32_t np = (w1 - w0) * k;
-                for (int32_t j = threadIdx.x; j < np; j += TD) {
-                    const int64_t src = ((int64_t)(w0 + j / k) * nb + bk) * k + j % k;
-                    pval[j] = values[src];
-                    pidx[j] = indices[src];
-                }
-                __syncthreads();
-                if (threadIdx.x < WAVE) {
-                    for (int32_t w = 0; w < w1 - w0; ++w) {
-                        if (lane_id() < k) {
-                            const uint32_t idx = pidx[w * k + lane_id()];
-                            if ((int64_t)idx < cnt) slice[idx] = slice[idx] + pval[w * k + lane_id()];
-                        }
-                    }
-                }
-                __syncthreads();
+        slice_init<TD>(acc, lo, cnt, slice, accumulate != 0);
+        __syncthreads();
+        for (int32_t w = 0; w < m; ++w) {
+            const int64_t base = ((int64_t)w * nb + bk) * k;
+            for (int64_t j = threadIdx.x; j < k; j += TD) {
+                const uint32_t idx = indices[base + j];
+                if ((int64_t)idx < cnt) slice[idx] = slice[idx] + values[base + j];
             }
-        } else {
-            __syncthreads();
-            for (int32_t w = 0; w < m; ++w) {
-                const int64_t base = ((int64_t)w * nb + bk) * k;
-                for (int64_t j = threadIdx.x; j < k; j += TD) {
-                    const uint32_t idx = indices[base + j];
-                    if ((int64_t)idx < cnt) slice[idx] = slice[idx] + values[base + j];
-                }
-                __syncthreads();  // worker w's additions land before worker w + 1's
-            }
+            __syncthreads();  // worker w's additions land before worker w + 1's
         }
-        slice_store(acc, lo, cnt, slice);
+        slice_store<TD>(acc, lo, cnt, slice);
         __syncthreads();
     }
+}
+
+// The sum for k < 64: one wave per bucket, its accumulator span in LDS.  The
+// wave takes the bucket's m*k pairs in chunks of SUM_CHUNK (worker-major
+// order, SUM_R per lane) and applies a chunk in sub-steps: every pending
+// pair raises its owner tag (a hash of its index) to (step << 8) | (255 -
+// its worker's rank in the chunk); the pairs holding the tag's value, i.e.
+// the lowest pending worker among those that share the tag, add their value
+// and leave.  The winners of a sub-step belong to one worker per tag, so
+// their indices are distinct and they add in parallel; for any one index
+// the additions happen in worker order, one sub-step after another.  A
+// wave's LDS instructions are carried out in program order, so each
+// sub-step sees the previous one's sums.  The number of sub-steps is the
+// largest number of workers sharing a tag; when that is large (workers
+// that chose the same indices) the protocol stops after a few sub-steps and
+// the rest of the chunk is applied one worker at a time.  The grid holds as
+// many one-wave blocks as fit at once, each working through its XCD's
+// share of the buckets with the next chunk's pairs in flight while one is
+// applied; neighbouring buckets run on the same XCD at about the same time,
+// since the 16-byte pieces of a worker's pairs for neighbouring buckets
+// share cache lines.
+__device__ __forceinline__ void wave_sync() {  // orders the lanes' LDS accesses before and after
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int SUM_R = 4;
+constexpr int SUM_CHUNK = SUM_R * WAVE;  // 256 pairs: a chunk spans at most 256 workers
+constexpr int SUM_TAGS = 1024;
+
+// One chunk's pairs for one lane: pair p = c + r*64 + lane of the bucket,
+// its worker's rank among the chunk's workers.
+struct SumPairs {
+    float val[SUM_R];
+    uint32_t idx[SUM_R], rank[SUM_R];
+};
+
+// Every lane issues all 2*SUM_R loads (pairs past the bucket's last read
+// element 0 and are dropped), so the number of loads in flight is fixed and
+// the wait for one chunk's pairs leaves the next chunk's loads outstanding.
+__device__ __forceinline__ void sum_fetch(const float* __restrict__ values, const uint32_t* __restrict__ indices,
+                                          int64_t nb, int32_t k, uint32_t total, int64_t bk, uint32_t c,
+                                          SumPairs& P) {
+    const uint32_t w0 = c / (uint32_t)k, r0 = c - w0 * (uint32_t)k;
+#pragma unroll
+    for (int r = 0; r < SUM_R; ++r) {
+        const uint32_t q = r0 + r * WAVE + lane_id();  // pair offset from worker w0's first pair
+        const uint32_t dw = q / (uint32_t)k;
+        const bool ok = c + r * WAVE + lane_id() < total;
+        const int64_t src = ok ? ((int64_t)(w0 + dw) * nb + bk) * k + (q - dw * (uint32_t)k) : 0;
+        const float v = values[src];
+        const uint32_t i = indices[src];
+        P.val[r] = ok ? v : 0.0f;
+        P.idx[r] = ok ? i : kNoIndex;
+        P.rank[r] = dw;
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Applies one chunk's pairs (held by one wave) to the slice, exactly in
+// worker order per index.  Up to SUM_TAG_STEPS sub-steps of the tag
+// protocol, then, for pairs still pending (many workers on the same
+// indices), one worker after another: after a sub-step, the pairs still
+// pending for an index all come from later workers than those applied.
+constexpr int SUM_TAG_STEPS = 4;
+
+__device__ __forceinline__ void sum_apply(const SumPairs& P, int64_t cnt, float* slice, uint32_t* tag,
+                                          uint32_t& step) {
+    bool pend[SUM_R];
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < SUM_R; ++r) {
+        pend[r] = (int64_t)P.idx[r] < cnt;
+        any = any || pend[r];
+    }
+    for (int sub = 0; sub < SUM_TAG_STEPS && __ballot(any) != 0; ++sub) {
+        ++step;
+        uint32_t mine[SUM_R], seen[SUM_R];
+        // raising a tag by 0 leaves it as it is: every lane takes part
+#pragma unroll
+        for (int r = 0; r < SUM_R; ++r) {
+            mine[r] = pend[r] ? (step << 8) | (255u - P.rank[r]) : 0u;
+            atomicMax(&tag[P.idx[r] & (SUM_TAGS - 1)], mine[r]);
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < SUM_R; ++r) seen[r] = tag[P.idx[r] & (SUM_TAGS - 1)];
+        bool win[SUM_R];
+        float old[SUM_R];
+#pragma unroll
+        for (int r = 0; r < SUM_R; ++r) {
+            win[r] = pend[r] && seen[r] == mine[r];
+            old[r] = slice[win[r] ? P.idx[r] : 0u];
+        }
+        wave_sync();
+        any = false;
+#pragma unroll
+        for (int r = 0; r < SUM_R; ++r) {
+            if (win[r]) slice[P.idx[r]] = old[r] + P.val[r];
+            pend[r] = pend[r] && !win[r];
+            any = any || pend[r];
+        }
+        wave_sync();
+    }
+    if (__ballot(any) != 0) {
+        uint32_t lo_rank = 0xFFFFFFFFu, hi_rank = 0u;
+#pragma unroll
+        for (int r = 0; r < SUM_R; ++r)
+            if (pend[r]) {
+                lo_rank = P.rank[r] < lo_rank ? P.rank[r] : lo_rank;
+                hi_rank = P.rank[r] > hi_rank ? P.rank[r] : hi_rank;
+            }
+        const uint32_t t1 = wave_max_u32(hi_rank);
+        // a worker's pairs have distinct indices: each step is one worker's
+        for (uint32_t t = wave_min_u32(lo_rank); t <= t1; ++t) {
+#pragma unroll
+            for (int r = 0; r < SUM_R; ++r)
+                if (pend[r] && P.rank[r] == t) slice[P.idx[r]] = slice[P.idx[r]] + P.val[r];
+            wave_sync();
+        }
+    }
+}
+
+// One chunk of a bucket: chunk 0 first sets up the slice and the tags, the
+// bucket's last chunk writes the slice out.
+__device__ __forceinline__ void sum_chunk(const SumPairs& P, float* __restrict__ acc, int64_t n, int32_t bucket,
+                                          uint32_t total, int32_t accumulate, int64_t bk, uint32_t c, float* slice,
+                                          uint32_t* tag, uint32_t& step) {
+    const int64_t lo = bk * bucket;
+    const int64_t cnt = n - lo < bucket ? n - lo : bucket;
+    if (c == 0) {
+        slice_init<WAVE>(acc, lo, cnt, slice, accumulate != 0);
+        for (int i = lane_id(); i < SUM_TAGS; i += WAVE) tag[i] = 0u;
+        step = 0;
+        wave_sync();
+    }
+    sum_apply(P, cnt, slice, tag, step);
+    if (c + SUM_CHUNK >= total) {
+        slice_store<WAVE>(acc, lo, cnt, slice);
+        wave_sync();  // the slice is rewritten by the next bucket
+    }
+}
+
+__global__ void __launch_bounds__(WAVE)
+k_topk_sum_wave(const float* __restrict__ values, const uint32_t* __restrict__ indices, int32_t m, int64_t n,
+                int64_t nb, int32_t bucket, int32_t k, float* __restrict__ acc, int32_t accumulate) {
+    extern __shared__ f32x4 lds4[];
+    float* slice = reinterpret_cast<float*>(lds4);
+    uint32_t* tag = reinterpret_cast<uint32_t*>(slice + bucket);  // bucket is a multiple of 64
+    const int64_t span = (nb + 7) / 8;                            // buckets of one XCD
+    const int64_t xcd = blockIdx.x & 7, stride = gridDim.x >> 3;  // gridDim.x is a multiple of 8
+    const int64_t end = (xcd + 1) * span < nb ? (xcd + 1) * span : nb;
+    const uint32_t total = (uint32_t)m * (uint32_t)k;             // pairs of a bucket, < 2^22
+
+    // The wave's work is a stream of (bucket, chunk) items; the pairs of the
+    // next item are in flight while one is applied, alternating between two
+    // register sets.  Past the last item the current one is fetched again,
+    // unused.
+    int64_t bk = xcd * span + (blockIdx.x >> 3);
+    uint32_t c = 0, step = 0;
+    if (bk >= end) return;
+    auto advance = [&](int64_t& b, uint32_t& ch) {
+        ch += SUM_CHUNK;
+        if (ch >= total) {
+            ch = 0;
+            b += stride;
+        }
+    };
+    SumPairs A, B;
+    sum_fetch(values, indices, nb, k, total, bk, c, A);
+    for (;;) {
+        int64_t bk1 = bk;
+        uint32_t c1 = c;
+        advance(bk1, c1);
+        const bool has1 = bk1 < end;
+        sum_fetch(values, indices, nb, k, total, has1 ? bk1 : bk, has1 ? c1 : c, B);
+        sum_chunk(A, acc, n, bucket, total, accumulate, bk, c, slice, tag, step);
+        if (!has1) break;
+        int64_t bk2 = bk1;
+        uint32_t c2 = c1;
+        advance(bk2, c2);
+        const bool has2 = bk2 < end;
+        sum_fetch(values, indices, nb, k, total, has2 ? bk2 : bk1, has2 ? c2 : c1, A);
+        sum_chunk(B, acc, n, bucket, total, accumulate, bk1, c1, slice, tag, step);
+        if (!has2) break;
+        bk = bk2;
+        c = c2;
+    }
+}
+
+constexpr int64_t kLdsPerCu = 160 * 1024;  // LDS of one gfx950 compute unit
+
+// Compute units of the current device, read once per device.  Only the
+// grid size depends on it.
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
 }
 
 template <int T, int EPT>
@@ -557,9 +758,20 @@ hipError_t launch_decode_topk(const float* values, const uint32_t* indices, int6
 hipError_t launch_topk_accumulate(const float* values, const uint32_t* indices, int32_t m, int64_t n,
                                   int32_t bucket, int32_t k, float* acc, bool accumulate, hipStream_t stream) {
     const int64_t nb = (n + bucket - 1) / bucket;
-    const size_t lds = (size_t)bucket * sizeof(float) + (size_t)PAIR_CAP * (sizeof(float) + sizeof(uint32_t));
-    hipLaunchKernelGGL(k_topk_accumulate, dim3((unsigned)grid_for(nb, 1)), dim3(TD), lds, stream, values, indices, m,
-                       n, nb, bucket, k, acc, accumulate ? 1 : 0);
+    if (k < WAVE) {
+        // as many one-wave blocks as the LDS of the CUs holds at once, each
+        // taking its XCD's buckets in turn
+        const size_t lds = (size_t)bucket * sizeof(float) + SUM_TAGS * sizeof(uint32_t);
+        const int64_t resident = (int64_t)cu_count() * (int64_t)(kLdsPerCu / lds);
+        const int64_t want = nb < resident ? nb : resident;
+        const int64_t grid = 8 * ((want + 7) / 8);
+        hipLaunchKernelGGL(k_topk_sum_wave, dim3((unsigned)grid), dim3(WAVE), lds, stream, values, indices, m, n, nb,
+                           bucket, k, acc, accumulate ? 1 : 0);
+    } else {
+        const size_t lds = (size_t)bucket * sizeof(float);
+        hipLaunchKernelGGL(k_topk_accumulate, dim3((unsigned)grid_for(nb, 1)), dim3(TD), lds, stream, values,
+                           indices, m, n, nb, bucket, k, acc, accumulate ? 1 : 0);
+    }
     return hipGetLastError();
 }
 

@@ -166,3 +166,59 @@ def test_topk_random_shapes(qc, ora):
         assert bits_equal(idx.host().view(np.uint32), pi), (trial, n, bucket, k)
         assert bits_equal(vals.f32(), pv), (trial, n, bucket, k)
         assert bits_equal(ef_d.f32(), ef_h), (trial, n, bucket, k)
+
+
+def sparse_workers(m, n, bucket, k, rng, mode):
+    """m workers' pairs for the sum.  mode "random": independent gradients;
+    "same": every worker sends the same indices (each index is hit m
+    times); "alias": indices that agree modulo 1024; "mixed": some
+    workers share indices, some do not, some slots are unused."""
+    nb = -(-n // bucket)
+    V = np.zeros((m, nb * k), np.float32)
+    I = np.full((m, nb * k), 0xFFFFFFFF, np.uint32)
+    for b in range(nb):
+        cnt = min(bucket, n - b * bucket)
+        kb = min(k, cnt)
+        common = rng.choice(cnt, kb, replace=False)
+        for w in range(m):
+            if mode == "same":
+                pick = common
+            elif mode == "alias":
+                base = rng.integers(0, min(cnt, 1024))
+                pick = np.unique((base + 1024 * np.arange(kb)) % cnt)[:kb]
+            elif mode == "mixed" and w % 3:
+                pick = common if w % 2 else rng.choice(cnt, kb, replace=False)
+                pick = pick[: kb - (w % 2)] if kb > 1 else pick
+            else:
+                pick = rng.choice(cnt, kb, replace=False)
+            pick = np.sort(pick)
+            vals = synth.host_normal(pick.size, 1.0, seed=int(rng.integers(1 << 30)))
+            vals[::5] = -0.0
+            V[w, b * k: b * k + pick.size] = vals
+            I[w, b * k: b * k + pick.size] = pick
+    return V.reshape(-1), I.reshape(-1)
+
+
+@pytest.mark.parametrize("mode", ["random", "same", "alias", "mixed"])
+@pytest.mark.parametrize("bucket,k,m,nbk", [(64, 1, 600, 3), (256, 63, 9, 9), (1024, 10, 100, 17),
+                                            (4096, 4, 64, 5), (8192, 33, 20, 2), (2048, 1, 3, 1)])
+def test_topk_sum_conflicts(qc, ora, mode, bucket, k, m, nbk):
+    """The one-wave sum for k < 64: several chunks of 256 pairs per bucket,
+    one worker per pair (k = 1, 600 workers), every worker on the same
+    indices, indices equal modulo the tag table's size, fewer buckets than
+    XCDs, a short last bucket, and a continued sum."""
+    rng = np.random.default_rng(bucket + k + m + len(mode))
+    n = nbk * bucket - (bucket // 3 if nbk > 1 else 0)
+    V, I = sparse_workers(m, n, bucket, k, rng, mode)
+    acc = out_f32(n)
+    qc.qc_topk_accumulate(dev(V), dev(I.view(np.int32)), m, n, bucket, k, acc.t, False)
+    sync()
+    want = ora.topk_accumulate(V, I, m, n, bucket, k)
+    assert bits_equal(acc.f32(), want), first_diff(acc.f32(), want)
+    start = synth.host_normal(n, 1.0, seed=m)
+    start[::7] = -0.0
+    acc.t.copy_(dev(start))
+    qc.qc_topk_accumulate(dev(V), dev(I.view(np.int32)), m, n, bucket, k, acc.t, True)
+    sync()
+    want2 = ora.topk_accumulate(V, I, m, n, bucket, k, acc=start)
+    assert bits_equal(acc.f32(), want2), first_diff(acc.f32(), want2)
