@@ -6,7 +6,7 @@
 // INT8/FP8 codes per worker, 8 bytes for 4-bit, 2 bytes for sign) and keeps
 // their fp32 sums in registers while it walks the workers in order, so the
 // result is bit-identical to adding the decoded terms one worker at a time.
-// Loads for UW workers are issued before their terms are added.  A bucket
+// Two workers' loads are kept in flight while terms are added.  A bucket
 // (group) is held by LPB lanes x K chunks x W waves (the layout of
 // qc_bucket.hpp with E = 16), which is what the fused requantization needs
 // to reduce min/max over the bucket without a second pass over acc.
@@ -262,42 +262,56 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
     }
 
     // Workers are taken 64 at a time (the statistics of one chunk of workers
-    // fit one register across the wave).  Within a chunk, UW register slots
+    // fit one register across the wave).  Within a chunk UW register slots
     // form a rolling prefetch: as soon as worker w's terms have been added
-    // (in worker order), its slot is refilled with worker w+UW, so every
-    // wave always has UW workers' code loads in flight while it computes.
-    // The refill clamps the worker index to the chunk's last worker, so it
-    // needs no branch; the repeated loads past the end are never added.
+    // (in worker order), its slot is refilled with worker w+UW, so every wave
+    // always has UW workers' code loads in flight while it computes.  The
+    // steady-state loop takes UW workers at a time and holds no branch (with the
+    // adds under a condition, the compiler moved each refill into the
+    // conditional block that used it, right before its wait), and a
+    // scheduling barrier after each refill keeps the instruction scheduler
+    // from moving it down next to its use to shorten register live ranges:
+    // either way the prefetch was lost.  The last (chunk size % UW) workers
+    // are added after the loop, from the slots that already hold them.
+    // Refills clamp the worker index to the chunk's last worker; the
+    // repeated loads past the end are never added.
     constexpr int32_t CHUNK = Stats<G, F>::WAVE_UNIFORM ? WAVE : 0x7FFFFFFF;
     Stats<G, F> st;
+    auto add_worker = [&](int32_t w, const ChunkBits<F> (&c)[K]) {
+        float s, z;
+        st.get(scale, zero, nb, bk, w, s, z);
+        if constexpr (F == A_QSGD) z = s / 7.0f;
+        if (needs_exact_path<F>(s, z)) {
+            if constexpr (F == A_QSGD || F == A_TER) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) add_chunk_exact<F>(a[k], c[k], s, z);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) add_chunk<F>(a[k], c[k], s, z);
+        }
+    };
     for (int32_t c0 = 0; c0 < m; c0 += CHUNK) {
         const int32_t cend = m - c0 > CHUNK ? c0 + CHUNK : m;
+        const int32_t last = cend - 1;
         st.load_chunk_of_workers(scale, zero, nb, bk, c0, cend);
         ChunkBits<F> slot[UW][K];
 #pragma unroll
         for (int u = 0; u < UW; ++u)
-            load_codes<G, F, FULL>(codes, pbytes, base, n, c0 + u < cend ? c0 + u : cend - 1, slot[u]);
-        for (int32_t w0 = c0; w0 < cend; w0 += UW) {
+            load_codes<G, F, FULL>(codes, pbytes, base, n, c0 + u < last ? c0 + u : last, slot[u]);
+        int32_t w0 = c0;
+        for (; w0 + UW <= cend; w0 += UW) {
 #pragma unroll
             for (int u = 0; u < UW; ++u) {
-                if (w0 + u < cend) {
-                    float s, z;
-                    st.get(scale, zero, nb, bk, w0 + u, s, z);
-                    if constexpr (F == A_QSGD) z = s / 7.0f;
-                    if (needs_exact_path<F>(s, z)) {
-                        if constexpr (F == A_QSGD || F == A_TER) {
-#pragma unroll
-                            for (int k = 0; k < K; ++k) add_chunk_exact<F>(a[k], slot[u][k], s, z);
-                        }
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < K; ++k) add_chunk<F>(a[k], slot[u][k], s, z);
-                    }
-                }
-                const int32_t w = w0 + UW + u < cend ? w0 + UW + u : cend - 1;
-                load_codes<G, F, FULL>(codes, pbytes, base, n, w, slot[u]);
+                add_worker(w0 + u, slot[u]);
+                const int32_t w = w0 + u + UW;
+                load_codes<G, F, FULL>(codes, pbytes, base, n, w < last ? w : last, slot[u]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+#pragma unroll
+        for (int u = 0; u < UW - 1; ++u)
+            if (w0 + u < cend) add_worker(w0 + u, slot[u]);
     }
 
     // acc is written with plain stores: a lane's 16 sums are 64 contiguous

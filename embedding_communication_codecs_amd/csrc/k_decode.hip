@@ -5,7 +5,10 @@
 // writes 2-32x more bytes than it reads).  A lane reads the 32-bit code
 // word holding its chunk (neighbouring lanes share a word for the sub-byte
 // formats; those repeats hit in L1) and the chunk's bucket statistics.
-// Each thread handles U chunks per tile, issuing all loads first.
+// Each thread handles U chunks per tile, issuing all loads first: U = 2
+// for a flat output (measured on MI355X: 5-20% faster than U = 4, most for
+// the 1-bit decoder; U = 1 and U = 8 are slower), U = 4 for a tensor list,
+// whose per-tile table search is then paid half as often.
 //
 // Bounds: the word holding a chunk that starts below n lies inside the
 // 16-byte-padded payload, so no read goes past the caller's buffer.
@@ -66,6 +69,7 @@ __device__ __forceinline__ float chunk_value(uint32_t w, int j, float s, float z
 // per tile with the tile's element range.
 
 struct FlatOut {
+    static constexpr int TILE_CHUNKS = 2;
     float* __restrict__ out;
     __device__ __forceinline__ void prepare(int64_t, int64_t) {}
     template <bool FULL>
@@ -103,6 +107,7 @@ __device__ __forceinline__ void tensor_range(const int64_t* __restrict__ off, co
 }
 
 struct TensorOuts {
+    static constexpr int TILE_CHUNKS = 4;
     float* const* __restrict__ outs;
     const int64_t* __restrict__ off;
     const int32_t* __restrict__ seg;
@@ -129,6 +134,19 @@ struct TensorOuts {
     }
 };
 
+// d = fl(a/7) without a division: q0 = fl(a * fl(1/7)), then one correction
+// with the exact remainder fma(-7, q0, a).  For every finite a this equals
+// the correctly rounded quotient (checked over all 2^32 bit patterns); when
+// q0 is a zero, an infinity or NaN it already is the quotient's value (a
+// zero q0 means |a/7| is at most half the smallest subnormal, since fl(1/7)
+// exceeds 1/7).
+__device__ __forceinline__ float div7(float a) {
+    constexpr float r7 = 0x1.24924ap-3f;
+    const float q0 = a * r7;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-7.0f, q0, a), r7, q0);
+    return (q0 == 0.0f || !__builtin_isfinite(q0)) ? q0 : q1;
+}
+
 template <int F, bool POW2, int U, bool FULL, class Dst>
 __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
                                             const float* __restrict__ zero, int64_t n, int64_t nchunks,
@@ -152,7 +170,7 @@ __device__ __forceinline__ void decode_tile(const uint8_t* __restrict__ codes, c
     for (int u = 0; u < U; ++u) {
         const int64_t c = t0 + u * 256 + threadIdx.x;
         if (!FULL && c >= nchunks) continue;
-        if constexpr (F == F_QSGD) z[u] = s[u] / 7.0f;
+        if constexpr (F == F_QSGD) z[u] = div7(s[u]);
         float o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = chunk_value<F>(w[u], j, s[u], z[u]);
@@ -181,7 +199,8 @@ k_decode(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
 template <int F, bool POW2, class Dst>
 hipError_t launch(const void* codes, const float* scale, const float* zero, int64_t n, int32_t group,
                   Dst dst, hipStream_t stream) {
-    constexpr int U = 4;
+    // a tensor-list output pays a table search per tile: longer tiles there
+    constexpr int U = Dst::TILE_CHUNKS;
     const int64_t nchunks = (n + 3) / 4;
     const dim3 grid((unsigned)grid_for(nchunks, 256 * U)), block(256);
     hipLaunchKernelGGL((k_decode<F, POW2, U, Dst>), grid, block, 0, stream, (const uint8_t*)codes, scale,

@@ -6,7 +6,9 @@
 // (for dim = 128: 2 rows, 1 KiB contiguous); RG such row groups are loaded
 // before any is processed to keep enough bytes in flight.  Other dims
 // (multiples of 4) take one wave per row and read the row twice (the second
-// read hits L2).
+// read hits L2).  The power-of-two dims compute the scale and codes without
+// dividing (exact shortcuts, below) and divide only where a shortcut does
+// not apply: the division was the encoder's main ALU cost.
 #include "qc_device.hpp"
 #include "qc_bucket.hpp"
 #include "qc_launch.hpp"
@@ -14,16 +16,61 @@
 namespace qc {
 namespace {
 
-__device__ __forceinline__ uint32_t fp8_pack4(f32x4 v, float sc) {
+// Exact forms: sc = fl(amax/448); code = e4m3(clamp(fl(x/sc), +-448)).
+__device__ __forceinline__ uint32_t fp8_pack4_exact(f32x4 v, float sc) {
     if (sc == 0.0f) return 0u;
     const float x[4] = {v.x, v.y, v.z, v.w};
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float y = fminf(fmaxf(x[j] / sc, -448.0f), 448.0f);
-        word |= e4m3_encode(y) << (8 * j);
-    }
+    for (int j = 0; j < 4; ++j) word |= e4m3_encode(fminf(fmaxf(x[j] / sc, -448.0f), 448.0f)) << (8 * j);
     return word;
+}
+
+// The same results without a division, for all but rare inputs; `fix` is
+// set where the shortcut does not apply, and the caller then redoes the
+// row group with the exact forms.
+//
+// Row scale: q0 = fl(amax * fl(1/448)) and one correction with the exact
+// remainder fma(-448, q0, amax).  For every amax from 2^-120 up to the
+// largest float this equals the correctly rounded quotient (checked over
+// all of them); other amax are fixed up.
+__device__ __forceinline__ float fp8_row_scale_fast(float amax, bool& fix) {
+    constexpr float r448 = 0x1.24924ap-9f;
+    fix |= !(amax >= 0x1p-120f && amax <= 0x1.fffffep127f);
+    const float q0 = amax * r448;
+    return __builtin_fmaf(__builtin_fmaf(-448.0f, q0, amax), r448, q0);
+}
+
+// Codes: y = fl(x/sc) matters only through its E4M3 rounding.  r
+// approximates 1/sc (hardware reciprocal, good to 1 ulp, and one Newton
+// step: relative error about 2^-24, far below 2^-22), so q = fl(x*r) rounds
+// a point within x/sc * 2^-22, i.e. less than 4 fp32 ulps, of x/sc;
+// rounding is monotone, so q and y are at most 4 ulps apart (8 across a
+// binade edge, where no E4M3 rounding point lies).  For |q| >= 2^-6 the
+// E4M3 code steps only where the 20 discarded mantissa bits of |y| pass
+// 0x80000, so when those bits of q differ from 0x80000 by more than 8 the
+// codes of q and y are equal (clamping at 448 is monotone too).  Values
+// below 2^-6, values near a rounding point and subnormal scales are fixed
+// up.  A zero scale gives code 0 either way.
+__device__ __forceinline__ uint32_t fp8_pack4_fast(f32x4 v, float sc, bool& fix) {
+    const float r0 = __builtin_amdgcn_rcpf(sc);
+    const float r = __builtin_fmaf(__builtin_fmaf(-sc, r0, 1.0f), r0, r0);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    float y[4];
+    uint32_t near[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        y[j] = x[j] * r;
+        // |D - 0x80000| <= 8 maps to [0, 16], D the discarded bits
+        near[j] = (__float_as_uint(y[j]) - 0x7FFF8u) & 0xFFFFFu;
+    }
+    const uint32_t nmin = min(min(near[0], near[1]), min(near[2], near[3]));
+    const float ymin = fminf(fminf(fabsf(y[0]), fabsf(y[1])), fminf(fabsf(y[2]), fabsf(y[3])));
+    fix |= sc != 0.0f && (nmin <= 16u || ymin < 0x1p-6f || !(sc >= 0x1p-126f));
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= e4m3_encode(fminf(fmaxf(y[j], -448.0f), 448.0f)) << (8 * j);
+    return sc == 0.0f ? 0u : word;
 }
 
 __device__ __forceinline__ float amax4(f32x4 v) {
@@ -49,16 +96,37 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
         const int64_t row = r0 + g * RPG + rsub;
         v[g] = (FULL || row < rows) ? ld_stream_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // every row group through the division-free forms first, branch-free,
+    // then one rarely taken branch redoes the lane's groups exactly if any
+    // needed it: amax is kept (no cross-lane work inside the branch) and the
+    // values are read again (an L2 hit) rather than kept in registers.
+    // (74 VGPRs, 6 waves per SIMD; forcing 8 waves spills to scratch, which
+    // measured 25% slower right after a write-heavy kernel.)
+    float amax[RG], sc[RG];
+    uint32_t word[RG];
+    bool fix = false;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        amax[g] = group_max<LPR>(amax4(v[g]));
+        sc[g] = fp8_row_scale_fast(amax[g], fix);
+        word[g] = fp8_pack4_fast(v[g], sc[g], fix);
+    }
+    if (__builtin_expect(fix, 0)) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int64_t row = r0 + g * RPG + rsub;
+            const f32x4 vg = (FULL || row < rows) ? ld_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            sc[g] = amax[g] / 448.0f;
+            word[g] = fp8_pack4_exact(vg, sc[g]);
+        }
+    }
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
         const int64_t row = r0 + g * RPG + rsub;
-        const float amax = group_max<LPR>(amax4(v[g]));
-        const float sc = amax / 448.0f;
-        const uint32_t word = fp8_pack4(v[g], sc);
         if (FULL || row < rows) {
-            st_u32(codes + row * DIM + l * 4, word);
+            st_u32(codes + row * DIM + l * 4, word[g]);
             if (l == 0) {
-                scale[row] = sc;
+                scale[row] = sc[g];
                 if (row == rows - 1) fp8_zero_tail(codes, rows * DIM, pbytes);
             }
         }
@@ -93,7 +161,7 @@ k_enc_fp8_rowwave(const float* __restrict__ x, int64_t rows, int32_t dim, uint8_
         amax = group_max<WAVE>(amax);
         const float sc = amax / 448.0f;
         for (int c = lane_id(); c < chunks; c += WAVE)
-            st_u32(codes + row * dim + 4 * c, fp8_pack4(ld_f4(xr + 4 * c), sc));
+            st_u32(codes + row * dim + 4 * c, fp8_pack4_exact(ld_f4(xr + 4 * c), sc));
         if (lane_id() == 0) {
             scale[row] = sc;
             if (row == rows - 1) fp8_zero_tail(codes, rows * dim, pbytes);

@@ -161,6 +161,57 @@ def test_fp8_conversion_sweep(qc, ora, seed):
     assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
 
 
+def test_fp8_quotients_near_rounding_points(qc, ora):
+    """Rows with scales of many magnitudes whose quotients x/scale fall
+    within a few ulps of every E4M3 rounding point (the encoder divides
+    exactly only there), plus rows with subnormal scales."""
+    dim = 256
+    rng = np.random.default_rng(77)
+    v = [m * 2.0 ** -9 for m in range(8)] + [(1 + m / 8) * 2.0 ** e for e in range(-6, 9) for m in range(8)]
+    v = np.array(sorted(set(x for x in v if x <= 448)))
+    mids = (v[:-1] + v[1:]) / 2
+    rows = []
+    for r in range(96):
+        e = int(rng.integers(-140, 120)) if r % 8 else int(rng.integers(-149, -130))
+        amax = np.float32(np.ldexp(rng.uniform(1, 2), e))
+        if amax == 0:
+            amax = np.float32(2.0 ** -149)
+        sc = np.float32(amax / np.float32(448))
+        pick = rng.choice(mids, dim - 1)
+        t = (pick * np.float64(sc)).astype(np.float32)
+        k = rng.integers(-6, 7, dim - 1)
+        for _ in range(6):
+            step = np.abs(k) > _
+            t = np.where(step, np.nextafter(t, np.where(k >= 0, np.inf, -np.inf).astype(np.float32)), t)
+        t = np.minimum(np.abs(t), amax) * np.where(rng.integers(0, 2, dim - 1) == 1, -1, 1)
+        rows.append(np.concatenate([[amax], t]).astype(np.float32))
+    x = np.concatenate(rows).astype(np.float32)
+    codes, scale = run_fp8(qc, x, 96, dim)
+    p, s = ora.encode_fp8_rowwise(x, 96, dim)
+    assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+
+
+def test_qsgd_decode_norm_bit_patterns(qc, ora):
+    """The decoder's step d = norm/7 for norms spread over every binade,
+    subnormals, zeros and infinities (the decoder takes them as given)."""
+    rng = np.random.default_rng(8)
+    nb, bucket = 1 << 16, 64
+    bits = rng.integers(0, 0x7F800000, nb, dtype=np.uint32)
+    bits[:256] = np.arange(256, dtype=np.uint32)  # zero and the smallest subnormals
+    bits[256:512] = 0x00800000 - np.arange(256, dtype=np.uint32)
+    bits[512:520] = [0x7F800000, 0x7F7FFFFF, 0x80000000, 0xFF800000, 0x80000001, 0xBF800000, 0x3F800000,
+                     0x40E00000]
+    norm = bits.view(np.float32)
+    n = nb * bucket
+    payload = rng.integers(0, 256, qc.payload_bytes(qc.QC_QSGD, n, bucket, 16), dtype=np.uint8)
+    out = out_f32(n)
+    qc.qc_decode(qc.QC_QSGD, dev(payload), dev(norm), None, n, bucket, 16, out.t)
+    sync()
+    want = ora.decode_qsgd(payload, norm, n, bucket)
+    assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
+
+
 # =================================================================== qsgd
 
 

@@ -1,0 +1,184 @@
+"""Host checks of two arithmetic shortcuts the GPU kernels take, each
+claimed to give exactly the result of the plain formula:
+
+* the QSGD decoder's step size d = fl(norm / 7) computed without a
+  division, as one multiplication by fl(1/7) and one correction with the
+  exact remainder (checked here over every fp32 bit pattern);
+* the rowwise FP8 encoder's row scale fl(amax / 448), computed the same
+  way for amax >= 2^-120 (checked over every such fp32 value);
+* the rowwise FP8 encoder's E4M3 code of fl(x / scale), computed from
+  fl(x * r) with r within an ulp of 1/scale, except where that product lies
+  within 8 ulps of an E4M3 rounding point or below 2^-6 (checked here on
+  crafted quotients that straddle every rounding point, with r one ulp off
+  either way, against the code of the true quotient).
+
+Both are the formulas as the kernels write them, evaluated with IEEE fp32
+arithmetic on the host (numpy float32; C fmaf)."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+DIV7_C = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+static float f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+static uint32_t b(float x) { uint32_t v; memcpy(&v, &x, 4); return v; }
+int main(void) {
+    const float r7 = 0x1.24924ap-3f;
+    unsigned long long bad = 0;
+    #pragma omp parallel for reduction(+:bad) schedule(static)
+    for (long long i = 0; i < (1LL << 32); ++i) {
+        const float a = f((uint32_t)i);
+        const float want = a / 7.0f;
+        const float q0 = a * r7;
+        const float q1 = fmaf(fmaf(-7.0f, q0, a), r7, q0);
+        const float got = (q0 == 0.0f || !isfinite(q0)) ? q0 : q1;
+        if (isnan(want) ? !isnan(got) : b(got) != b(want)) ++bad;
+    }
+    printf("%llu\n", bad);
+    return 0;
+}
+"""
+
+
+DIV448_C = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+static float f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+static uint32_t b(float x) { uint32_t v; memcpy(&v, &x, 4); return v; }
+int main(void) {
+    const float r448 = 0x1.24924ap-9f;
+    unsigned long long bad = 0;
+    #pragma omp parallel for reduction(+:bad) schedule(static)
+    for (long long i = 0; i < (1LL << 32); ++i) {
+        const float a = f((uint32_t)i);
+        const float want = a / 448.0f;
+        float got;
+        if (!(a >= 0x1p-120f && a <= 0x1.fffffep127f)) {
+            got = a / 448.0f;
+        } else {
+            const float q0 = a * r448;
+            got = fmaf(fmaf(-448.0f, q0, a), r448, q0);
+        }
+        if (isnan(want) ? !isnan(got) : b(got) != b(want)) ++bad;
+    }
+    printf("%llu\n", bad);
+    return 0;
+}
+"""
+
+
+def run_c(src_text):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    d = tempfile.mkdtemp()
+    try:
+        src, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        with open(src, "w") as fh:
+            fh.write(src_text)
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", src, "-o", exe, "-lm"], check=True,
+                       capture_output=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True,
+                             env={**os.environ, "OMP_NUM_THREADS": str(min(8, os.cpu_count() or 1))})
+        return int(out.stdout.strip())
+    finally:
+        shutil.rmtree(d)
+
+
+@pytest.mark.slow
+def test_div448_every_float():
+    """fl(1/448) is 0x1.24924ap-9; the corrected product is the correctly
+    rounded amax/448 wherever the kernel uses it (amax in [2^-120, max])."""
+    assert np.float32(1.0) / np.float32(448.0) == np.float32(float.fromhex("0x1.24924ap-9"))
+    assert run_c(DIV448_C) == 0
+
+
+@pytest.mark.slow
+def test_div7_every_float():
+    """fl(1/7) is 0x1.24924ap-3 and the corrected product equals the
+    correctly rounded a/7 for all 2^32 inputs (zeros, subnormals,
+    infinities and NaN included)."""
+    assert np.float32(1.0) / np.float32(7.0) == np.float32(float.fromhex("0x1.24924ap-3"))
+    assert run_c(DIV7_C) == 0
+
+
+def e4m3_midpoints():
+    """Every point where round-to-nearest-even to E4M3 changes its result,
+    for magnitudes in (0, 448): halfway between neighbouring codes."""
+    vals = [m * 2.0 ** -9 for m in range(8)]  # subnormals
+    for e in range(-6, 9):
+        for m in range(8):
+            v = (1 + m / 8) * 2.0 ** e
+            if v <= 448:
+                vals.append(v)
+    vals = np.array(sorted(set(vals)))
+    return (vals[:-1] + vals[1:]) / 2
+
+
+def fast_code(ora, x, sc, r=None, window=8):
+    """The kernel's path: q = fl(x * r), r ~ 1/sc; the division when q is
+    below 2^-6 or its discarded bits are within `window` of the rounding
+    point (or sc is subnormal)."""
+    if r is None:
+        r = np.float32(1.0) / sc
+    q = (x * r).astype(np.float32)
+    near = (q.view(np.uint32) - np.uint32(0x80000 - window)) & np.uint32(0xFFFFF)
+    exact = (np.abs(q) < np.float32(2.0 ** -6)) | (near <= 2 * window) | (sc < np.float32(2.0 ** -126))
+    y = np.where(exact, (x / sc).astype(np.float32), q).astype(np.float32)
+    y = np.clip(y, np.float32(-448), np.float32(448))
+    return ora.e4m3_from_f32_n(y), exact
+
+
+def reciprocals(sc):
+    """fl(1/sc) and its two neighbours: the kernel's reciprocal is within
+    one ulp of the true 1/sc."""
+    r = np.float32(1.0) / sc
+    return [r, np.nextafter(r, np.float32(np.inf)), np.nextafter(r, np.float32(0))]
+
+
+def test_fp8_reciprocal_path_matches_division(ora):
+    rng = np.random.default_rng(11)
+    mids = e4m3_midpoints()
+    checked = fast_hits = 0
+    for trial in range(200):
+        # a row scale of any magnitude: amax / 448 for a random amax
+        amax = np.float32(np.ldexp(rng.uniform(1, 2), int(rng.integers(-100, 100))))
+        sc = np.float32(amax / np.float32(448))
+        # values whose quotient is within +-24 ulps of each rounding point,
+        # both signs, plus uniform values over the row's range
+        t = (mids.astype(np.float64) * np.float64(sc)).astype(np.float32)
+        k = rng.integers(-24, 25, t.size)
+        x = np.nextafter(t, np.where(k >= 0, np.inf, -np.inf).astype(np.float32))
+        for _ in range(3):
+            step = np.abs(k) > _
+            x = np.where(step, np.nextafter(x, np.where(k >= 0, np.inf, -np.inf).astype(np.float32)), x)
+        x = np.concatenate([x, -x, rng.uniform(-1, 1, 4096).astype(np.float32) * amax, [amax, -amax]])
+        x = x.astype(np.float32)
+        want = ora.e4m3_from_f32_n(np.clip((x / sc).astype(np.float32), np.float32(-448), np.float32(448)))
+        for r in reciprocals(sc):
+            got, exact = fast_code(ora, x, sc, r)
+            assert np.array_equal(got, want), trial
+            checked += x.size
+            fast_hits += int((~exact).sum())
+    assert fast_hits > 0.8 * checked  # the shortcut is the common path
+
+
+def test_fp8_reciprocal_path_differs_from_division_in_the_quotient(ora):
+    """The shortcut is not an identity on fp32: the product and the
+    quotient differ for many elements, only their codes agree."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(1 << 16).astype(np.float32)
+    sc = np.float32(np.float32(np.abs(x).max()) / np.float32(448))
+    q = (x * (np.float32(1) / sc)).astype(np.float32)
+    y = (x / sc).astype(np.float32)
+    assert (q != y).sum() > 1000
+    got, _ = fast_code(ora, x, sc)
+    assert np.array_equal(got, ora.e4m3_from_f32_n(np.clip(y, np.float32(-448), np.float32(448))))
