@@ -622,8 +622,14 @@ hipError_t dispatch_bucket(int32_t bucket, F&& f) {
         case 64: return f(Geom<E, 64, 1, 1>{});
         case 128: return f(Geom<E, 64, 2, 1>{});
         case 256: return f(Geom<E, 64, 4, 1>{});
-        case 512: return f(Geom<E, 64, 8, 1>{});
-        case 1024: return f(Geom<E, 64, 8, 2>{});
+        // E = 8 (the bf16 sign encoder): one chunk per lane over 8 waves; a
+        // whole bucket per wave needed 165 registers (3 waves per SIMD) and
+        // measured 5% slower on MI355X
+        case 512: if constexpr (E == 8) return f(Geom<E, 64, 1, 8>{}); else return f(Geom<E, 64, 8, 1>{});
+        // E = 4, buckets of 4096: two chunks per lane over 8 waves (8 chunks
+        // over 2 waves needed 117 registers, 4 waves per SIMD, and measured
+        // 5-6% slower on MI355X)
+        case 1024: if constexpr (E == 4) return f(Geom<E, 64, 2, 8>{}); else return f(Geom<E, 64, 8, 2>{});
         case 2048: return f(Geom<E, 64, 8, 4>{});
         case 4096: return f(Geom<E, 64, 8, 8>{});
         case 8192: return f(Geom<E, 64, 8, 16>{});
