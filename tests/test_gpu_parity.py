@@ -317,6 +317,42 @@ def test_sign_small_bucket_tails(qc, ora, n):
     assert bits_equal(scale.f32(), s)
 
 
+# Buckets of 4096 are spread over 8 waves (fp32: 2 chunks per lane; bf16
+# sign: 1 chunk per lane): a last bucket that ends inside any of the 8 waves
+# leaves later waves with no valid element, and they still take part in the
+# bucket's reductions.
+TAILS_4096 = [1, 300, 512, 513, 1500, 2048, 3000, 4095]
+
+
+@pytest.mark.parametrize("tail", TAILS_4096)
+def test_bucket_4096_tails_inside_every_wave(qc, ora, tail):
+    B = 4096
+    n = 2 * B + tail
+    g = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=77 + tail)
+    for bits in (8, 4):
+        ef_h = synth.host_normal(n, 1e-4, seed=tail)
+        ef_d = dev_ef(ef_h)
+        codes, scale, zero = run_uniform(qc, g, ef_d, B, bits)
+        p, s, z = ora.encode_uniform(g, ef_h, B, bits)
+        assert bits_equal(codes.host(), p), (bits, first_diff(codes.host(), p))
+        assert bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z), bits
+        assert bits_equal(ef_d.f32(), ef_h), (bits, first_diff(ef_d.f32(), ef_h))
+    ef_h = synth.host_normal(n, 1e-4, seed=tail + 1)
+    ef_d = dev_ef(ef_h)
+    words, norm = run_qsgd(qc, g, ef_d, B, 0x5153474400000001, 0)
+    p, nr = ora.encode_qsgd(g, ef_h, B, 0x5153474400000001, 0)
+    assert bits_equal(words.host(), p) and bits_equal(norm.f32(), nr), first_diff(words.host(), p)
+    assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    for x in (g, synth.host_bf16_bits(g)):
+        ef_h = synth.host_normal(n, 1e-4, seed=tail + 2)
+        ef_d = dev_ef(ef_h)
+        words, scale = run_sign(qc, x, ef_d, B)
+        p, s = ora.encode_sign(x, ef_h, B)
+        assert bits_equal(words.host(), p), (x.dtype, first_diff(words.host(), p))
+        assert bits_equal(scale.f32(), s), (x.dtype, first_diff(scale.f32(), s))
+        assert bits_equal(ef_d.f32(), ef_h), (x.dtype, first_diff(ef_d.f32(), ef_h))
+
+
 # ============================================================= accumulate
 
 

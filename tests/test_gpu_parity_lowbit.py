@@ -377,3 +377,24 @@ def test_qsgd_accumulate_with_overflowing_norm(qc, ora):
     qc.qc_dequant_accumulate(2, dev(payloads), dev(norm), None, m, n, B, 16, acc.t, True)
     sync()
     assert bits_or_both_nan(acc.f32(), want), first_diff(acc.f32(), want)
+
+
+@pytest.mark.parametrize("tail", [1, 513, 2048, 4095])
+def test_bucket_4096_tails_lowbit(qc, ora, tail):
+    """Stochastic 2-bit uniform and TernGrad with buckets of 4096 (8 waves
+    per bucket) and a last bucket ending inside different waves."""
+    B = 4096
+    n = 2 * B + tail
+    g = synth.host_laplace(n, 1e-4, seed=300 + tail)
+    ef_h = synth.host_normal(n, 1e-5, seed=tail)
+    ef_d = dev_ef(ef_h)
+    codes, scale, zero = run_uniform(qc, g, ef_d, B, 2, stochastic=True, seed=0x53544F43, offset=12344)
+    p, s, z = ora.encode_uniform_stochastic(g, ef_h, B, 2, 0x53544F43, 12344)
+    assert bits_equal(codes.host(), p) and bits_equal(scale.f32(), s) and bits_equal(zero.f32(), z)
+    assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+    ef_h = synth.host_normal(n, 1e-5, seed=tail + 1)
+    ef_d = dev_ef(ef_h)
+    words, scale = run_ternary(qc, g, ef_d, B, 0x5445524E, 8)
+    p, s = ora.encode_ternary(g, ef_h, B, 0x5445524E, 8)
+    assert bits_equal(words.host(), p) and bits_equal(scale.f32(), s), first_diff(words.host(), p)
+    assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)

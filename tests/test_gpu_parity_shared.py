@@ -216,3 +216,21 @@ def test_shared_chain_on_gpu_end_to_end(qc, ora):
     for w in range(m):
         assert bits_equal(efs_d[w].f32(), efs_h[w])
     assert bits_equal(out.cpu().numpy(), o_out), first_diff(out.cpu().numpy(), o_out)
+
+
+@pytest.mark.parametrize("tail", [1, 513, 2048, 4095])
+def test_bucket_4096_tails_shared(qc, ora, tail):
+    """The bucket statistic and the shared-scale encoder with buckets of
+    4096 (8 waves per bucket), last bucket ending inside different waves."""
+    B = 4096
+    n = 2 * B + tail
+    x = synth.host_outlier_grad(n, 1e-3, 0.01, 100.0, seed=500 + tail)
+    ef_h = synth.host_normal(n, 1e-4, seed=tail)
+    amax = gpu_absmax(qc, x, dev_ef(ef_h), B)
+    want = ora.bucket_absmax(x, ef_h, B)
+    assert bits_equal(amax.f32(), want), first_diff(amax.f32(), want)
+    ef_d = dev_ef(ef_h)
+    codes, scale = gpu_encode(qc, x, ef_d, B, want)
+    p, s = ora.encode_int8_shared(x, ef_h, B, want)
+    assert bits_equal(codes.host(), p) and bits_equal(scale.f32(), s), first_diff(codes.host(), p)
+    assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
