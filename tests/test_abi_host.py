@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -343,3 +344,21 @@ def test_topk_errors(qc):
     assert call(qc, f, A, A, 3, 1000, 512, 8, NULL, 0, None) == qc.QC_ERR_ARG
     assert call(qc, f, A, A, 3, 1000, 512, 8, MIS, 0, None) == qc.QC_ERR_ALIGN
     assert call(qc, f, NULL, NULL, 3, 0, 512, 8, NULL, 0, None) == qc.QC_OK
+
+
+def test_missing_library_fails_loudly():
+    """No CPU fallback: with libqc.so absent, the first call raises instead of
+    computing anything on the host."""
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import embedding_communication_codecs_amd.binding as b\n"
+        "b.LIB_PATH = '/nonexistent/libqc.so'\n"
+        "try:\n"
+        "    b.qc_payload_bytes(0, 1024, 64, 8)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised', 'missing' in str(e))\n"
+        "else:\n"
+        "    print('returned')\n" % ROOT
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.stdout.strip() == "raised True", r.stdout + r.stderr
