@@ -17,11 +17,14 @@ namespace qc {
 namespace {
 
 // Exact forms: sc = fl(amax/448); code = e4m3(clamp(fl(x/sc), +-448)).
+// Only the rare fallback below and odd dims use them, so the divisions run
+// one at a time (unrolled, four division sequences in flight held the
+// whole kernel at 82 registers and 5 waves per SIMD; rolled, 63 and 8).
 __device__ __forceinline__ uint32_t fp8_pack4_exact(f32x4 v, float sc) {
     if (sc == 0.0f) return 0u;
     const float x[4] = {v.x, v.y, v.z, v.w};
     uint32_t word = 0;
-#pragma unroll
+#pragma unroll 1
     for (int j = 0; j < 4; ++j) word |= e4m3_encode(fminf(fmaxf(x[j] / sc, -448.0f), 448.0f)) << (8 * j);
     return word;
 }
@@ -100,8 +103,8 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
     // then one rarely taken branch redoes the lane's groups exactly if any
     // needed it: amax is kept (no cross-lane work inside the branch) and the
     // values are read again (an L2 hit) rather than kept in registers.
-    // (74 VGPRs, 6 waves per SIMD; forcing 8 waves spills to scratch, which
-    // measured 25% slower right after a write-heavy kernel.)
+    // The fallback loop is not unrolled, so it adds nothing to the
+    // registers the fast path holds.
     float amax[RG], sc[RG];
     uint32_t word[RG];
     bool fix = false;
@@ -112,7 +115,7 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
         word[g] = fp8_pack4_fast(v[g], sc[g], fix);
     }
     if (__builtin_expect(fix, 0)) {
-#pragma unroll
+#pragma unroll 1
         for (int g = 0; g < RG; ++g) {
             const int64_t row = r0 + g * RPG + rsub;
             const f32x4 vg = (FULL || row < rows) ? ld_f4(x + row * DIM + l * 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -123,25 +126,57 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
         const int64_t row = r0 + g * RPG + rsub;
-        if (FULL || row < rows) {
-            st_u32(codes + row * DIM + l * 4, word[g]);
-            if (l == 0) {
-                scale[row] = sc[g];
-                if (row == rows - 1) fp8_zero_tail(codes, rows * DIM, pbytes);
-            }
+        if (FULL || row < rows) st_u32(codes + row * DIM + l * 4, word[g]);
+    }
+    if constexpr (FULL && LPR >= 16) {
+        // With few rows per load (dim >= 64) the wave's RPG*RG row scales
+        // are gathered with readlane (every lane of a row holds its row's
+        // scale) and written as whole 16-byte pieces, lane p writing rows
+        // 4p..4p+3 of the wave's consecutive rows.  (Written one 4-byte value
+        // per row, each went to HBM as its own partial write: 1.10x the
+        // algorithmic write bytes at dim 128.)  Smaller dims already store
+        // RPG >= 8 consecutive scales per instruction.
+        constexpr int RPW = RPG * RG;
+        float s[RPW];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int rs = 0; rs < RPG; ++rs)
+                s[g * RPG + rs] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[g]), rs * LPR));
+        const int p = lane_id();
+        if (p < RPW / 4) {
+            f32x4 o = f32x4{s[0], s[1], s[2], s[3]};
+#pragma unroll
+            for (int q = 1; q < RPW / 4; ++q)
+                if (p == q) o = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+            st_f4(scale + r0 + 4 * p, o);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int64_t row = r0 + g * RPG + rsub;
+            if ((FULL || row < rows) && l == 0) scale[row] = sc[g];
         }
     }
+    // the owner of the last row zeroes the payload's padding
+    if (lane_id() == 0 && r0 <= rows - 1 && rows - 1 < r0 + RPG * RG)
+        fp8_zero_tail(codes, rows * DIM, pbytes);
 }
 
 // Wave w of the grid handles RPW = RG * 64/LPR consecutive rows per
 // iteration; groups of rows wholly inside `rows` take the branch-free path.
+// Two waves per block and one short-lived wave per RPW rows measured best
+// on MI355X at 1e6 x 128: 4-wave blocks were 3% slower, 8-wave blocks 8%;
+// RG = 6 or 8 and persistent waves that load their next rows before
+// encoding the current ones were 5-25% slower; plain (not streaming) loads
+// were 50% slower right after a write-heavy kernel.
 template <int LPR, int RG>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(128)
 k_enc_fp8_pow2(const float* __restrict__ x, int64_t rows, uint8_t* __restrict__ codes,
                int64_t pbytes, float* __restrict__ scale) {
     constexpr int RPW = (WAVE / LPR) * RG;
-    const int64_t wstride = (int64_t)gridDim.x * 4;
-    for (int64_t r0 = ((int64_t)blockIdx.x * 4 + wave_id()) * RPW; r0 < rows; r0 += wstride * RPW) {
+    const int64_t wstride = (int64_t)gridDim.x * 2;
+    for (int64_t r0 = ((int64_t)blockIdx.x * 2 + wave_id()) * RPW; r0 < rows; r0 += wstride * RPW) {
         if (r0 + RPW <= rows)
             fp8_rows<LPR, RG, true>(x, rows, codes, pbytes, scale, r0);
         else
@@ -175,7 +210,7 @@ hipError_t launch_pow2(const float* x, int64_t rows, uint8_t* codes, int64_t pby
     constexpr int RG = 4;
     constexpr int RPW = (WAVE / LPR) * RG;
     const int64_t waves = (rows + RPW - 1) / RPW;
-    const dim3 grid((unsigned)grid_for(waves, 4)), block(256);
+    const dim3 grid((unsigned)grid_for(waves, 2)), block(128);
     hipLaunchKernelGGL((k_enc_fp8_pow2<LPR, RG>), grid, block, 0, stream, x, rows, codes, pbytes, scale);
     return hipGetLastError();
 }
