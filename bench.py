@@ -388,76 +388,107 @@ def make_ops(qc, st):
 # ----------------------------------------------------------- cpu baseline
 
 
+def host_cpu():
+    """The host's logical CPU count and CPU model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
 def cpu_baseline():
-    """The CPU oracle, single-threaded, on a bounded sample of each op."""
+    """The CPU oracle, single-threaded and pinned to one core, on a bounded
+    sample of each op of the step: input GB/s per op (same input-byte
+    accounting as the GPU figures) and over the whole sample."""
     import numpy as np
 
     import oracle as ora
     from embedding_communication_codecs_amd import synth
 
     ora.lib()
-    total_in, total_t = 0, 0.0
+    ncpu, model = host_cpu()
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    per_op = {}
 
-    def timed(fn):
+    def timed(op, in_bytes, sample, fn):
         t0 = time.perf_counter()
         r = fn()
-        return r, time.perf_counter() - t0
+        t = time.perf_counter() - t0
+        per_op[op] = {"GBps": round(in_bytes / t / 1e9, 4), "s": round(t, 3), "input_bytes": in_bytes,
+                      "sample": sample}
+        return r
 
-    # uniform (whole workload: it is small)
-    g = synth.host_normal(C1_N, 1e-3, 1001)
-    ef = np.zeros(C1_N, np.float32)
-    (p, s, z), t = timed(lambda: ora.encode_uniform(g, ef, C1_B, 8))
-    _, t2 = timed(lambda: ora.decode_uniform(p, s, z, C1_N, C1_B, 8))
-    total_in += 8 * C1_N
-    total_t += t + t2
-    # fp8: the whole 1,000,000 x 128 workload
-    rows = C2_ROWS
-    x = synth.host_embedding_rows(rows, C2_DIM, 0.05, 0.001, 50.0, 2001)
-    (p, s), t = timed(lambda: ora.encode_fp8_rowwise(x, rows, C2_DIM))
-    _, t2 = timed(lambda: ora.decode_fp8_rowwise(p, s, rows, C2_DIM))
-    total_in += 8 * rows * C2_DIM
-    total_t += t + t2
-    # qsgd: 128M elements
-    n3 = 1 << 27
-    x = synth.host_laplace(n3, 1e-4, 3001)
-    ef = np.zeros(n3, np.float32)
-    (p, s), t = timed(lambda: ora.encode_qsgd(x, ef, C3_B, 0x5153474400000001, 0))
-    _, t2 = timed(lambda: ora.decode_qsgd(p, s, n3, C3_B))
-    total_in += 8 * n3
-    total_t += t + t2
-    # sign: 128M bf16, vote over 16 payloads of 128M bits, decode
-    n4 = 1 << 27
-    gb = synth.host_bf16_bits(synth.host_normal(n4, 1e-3, 4001))
-    ef = np.zeros(n4, np.float32)
-    (p, s), t = timed(lambda: ora.encode_sign(gb, ef, C4_B))
-    pb = ora.payload_bytes(ora.SIGN, n4, 1)
-    arena = np.concatenate([synth.host_words(pb // 4, 4100 + w).view(np.uint8) for w in range(C4_M)])
-    _, t2 = timed(lambda: ora.majority_vote(arena, C4_M, n4))
-    _, t3 = timed(lambda: ora.decode_sign(p, s, n4, C4_B))
-    total_in += 2 * n4 + C4_M * pb + 4 * n4
-    total_t += t + t2 + t3
-    # accumulate: 64 workers x 4M elements, then requantize
-    n5 = 1 << 22
-    parts, scs, zes = [], [], []
-    for w in range(C5_M):
-        pp, ss, zz = ora.encode_uniform(synth.host_outlier_grad(n5, 1e-3, 0.01, 100.0, 5000 + w), None, C5_B, 8)
-        parts.append(pp)
-        scs.append(ss)
-        zes.append(zz)
-    arena, sc, ze = np.concatenate(parts), np.concatenate(scs), np.concatenate(zes)
-    acc, t = timed(lambda: ora.dequant_accumulate(ora.UNIFORM, arena, sc, ze, C5_M, n5, C5_B, 8))
-    _, t2 = timed(lambda: ora.encode_uniform(acc, None, C5_B, 8))
-    total_in += 4 * C5_M * n5
-    total_t += t + t2
+    try:
+        # uniform (whole workload: it is small)
+        g = synth.host_normal(C1_N, 1e-3, 1001)
+        ef = np.zeros(C1_N, np.float32)
+        p, s, z = timed("uniform_enc", 4 * C1_N, f"{C1_N} (whole)", lambda: ora.encode_uniform(g, ef, C1_B, 8))
+        timed("uniform_dec", 4 * C1_N, f"{C1_N} (whole)", lambda: ora.decode_uniform(p, s, z, C1_N, C1_B, 8))
+        # fp8: the whole 1,000,000 x 128 workload
+        rows = C2_ROWS
+        x = synth.host_embedding_rows(rows, C2_DIM, 0.05, 0.001, 50.0, 2001)
+        p, s = timed("fp8_enc", 4 * rows * C2_DIM, f"{rows}x{C2_DIM} (whole)",
+                     lambda: ora.encode_fp8_rowwise(x, rows, C2_DIM))
+        timed("fp8_dec", 4 * rows * C2_DIM, f"{rows}x{C2_DIM} (whole)",
+              lambda: ora.decode_fp8_rowwise(p, s, rows, C2_DIM))
+        del x
+        # qsgd: 2^27 elements
+        n3 = 1 << 27
+        x = synth.host_laplace(n3, 1e-4, 3001)
+        ef = np.zeros(n3, np.float32)
+        p, s = timed("qsgd_enc", 4 * n3, f"{n3} of {C3_N}",
+                     lambda: ora.encode_qsgd(x, ef, C3_B, 0x5153474400000001, 0))
+        timed("qsgd_dec", 4 * n3, f"{n3} of {C3_N}", lambda: ora.decode_qsgd(p, s, n3, C3_B))
+        del x, ef
+        # sign: 2^27 bf16, vote over 16 payloads of 2^27 bits, decode
+        n4 = 1 << 27
+        gb = synth.host_bf16_bits(synth.host_normal(n4, 1e-3, 4001))
+        ef = np.zeros(n4, np.float32)
+        p, s = timed("sign_enc", 2 * n4, f"{n4} of {C4_N}", lambda: ora.encode_sign(gb, ef, C4_B))
+        pb = ora.payload_bytes(ora.SIGN, n4, 1)
+        arena = np.concatenate([synth.host_words(pb // 4, 4100 + w).view(np.uint8) for w in range(C4_M)])
+        timed("sign_vote", C4_M * pb, f"{C4_M}x{n4} bits of {C4_M}x{C4_N}",
+              lambda: ora.majority_vote(arena, C4_M, n4))
+        timed("sign_dec", 4 * n4, f"{n4} of {C4_N}", lambda: ora.decode_sign(p, s, n4, C4_B))
+        del gb, ef, arena
+        # accumulate: 64 workers x 2^22 elements, then requantize
+        n5 = 1 << 22
+        parts, scs, zes = [], [], []
+        for w in range(C5_M):
+            pp, ss, zz = ora.encode_uniform(synth.host_outlier_grad(n5, 1e-3, 0.01, 100.0, 5000 + w), None, C5_B, 8)
+            parts.append(pp)
+            scs.append(ss)
+            zes.append(zz)
+        arena, sc, ze = np.concatenate(parts), np.concatenate(scs), np.concatenate(zes)
+
+        def acc_requant():
+            acc = ora.dequant_accumulate(ora.UNIFORM, arena, sc, ze, C5_M, n5, C5_B, 8)
+            return ora.encode_uniform(acc, None, C5_B, 8)
+
+        timed("acc_requant", 4 * C5_M * n5, f"{C5_M}x{n5} of {C5_M}x{C5_N}", acc_requant)
+    finally:
+        os.sched_setaffinity(0, old_aff)
+    total_in = sum(v["input_bytes"] for v in per_op.values())
+    total_t = sum(v["s"] for v in per_op.values())
     return {
         "value": round(total_in / total_t / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": ("every op of the step on a sample: uniform 65,536 (whole); fp8 1,000,000x128 (whole); "
-                   "qsgd 134,217,728; sign 134,217,728 bf16 + vote 16x134,217,728 bits + decode; "
-                   "accumulate 64x4,194,304 + requantize; single-threaded C oracle, same input-byte "
-                   f"accounting; {total_t:.1f} s of CPU time"),
+        "host_cpus": ncpu,
+        "host_cpu_model": model,
+        "pinned_core": core,
+        "sample": ("every op of the step on a sample (per_op gives each): single-threaded C oracle pinned to one "
+                   f"core of {ncpu}, same input-byte accounting as the GPU figures; {total_t:.1f} s of CPU time"),
+        "per_op": per_op,
     }
 
 
@@ -550,6 +581,28 @@ def time_ops(torch, ops, names, sizes, steps, warmup, extra):
     return wall_ms, per_op
 
 
+def time_alone(torch, ops, names, sizes, per_op, reps):
+    """Each op by itself: every launch starts on an idle GPU (synchronized
+    before it), so its time does not depend on what ran before it in the
+    step.  Adds ms_alone and hbm_frac_alone to per_op."""
+    stream = torch.cuda.current_stream()
+    for o in names:
+        ops[o]()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            ops[o]()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = sum(times) / reps
+        hbm = sizes[o][1]
+        per_op[o]["ms_alone"] = round(ms, 4)
+        per_op[o]["hbm_frac_alone"] = round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -603,10 +656,18 @@ def main():
     if ext_names:
         ext_ms, ext = time_ops(torch, ops, ext_names, sizes, args.steps, args.warmup, None)
         print(f"[bench] extensions timed ({ext_ms:.3f} ms per pass)", file=sys.stderr, flush=True)
+    time_alone(torch, ops, names, sizes, per_op, args.steps)
+    if ext is not None:
+        time_alone(torch, ops, ext_names, sizes, ext, args.steps)
+    print("[bench] each op timed alone", file=sys.stderr, flush=True)
     total_in = sum(sizes[o][0] for o in names)
     dom = max(names, key=lambda o: per_op[o]["ms"])
     achieved = per_op[dom]["hbm_GBps"]
     traffic = load_traffic(dom)
+    st.clear()
+    torch.cuda.empty_cache()
+    cal = calibrate(torch)
+    print("[bench] calibration copy/fill/read timed", file=sys.stderr, flush=True)
     result = {
         "metric": "codec GB/s (fp32 in, encode+EF / decode+accum) and % of MI355X HBM peak",
         "value": round(total_in / (ms_per_step * 1e-3) / 1e9, 2),
@@ -644,7 +705,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_source": (None if traffic is None else
+                               "cached: rocprofv3 FETCH_SIZE + WRITE_SIZE runs of this kernel source, "
+                               "profiles/pmc_traffic_codec_suite.json (dropped when the source changes)"),
         },
+        "calibration": cal,
         "ops": per_op,
     }
     if ext is not None:

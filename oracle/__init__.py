@@ -344,11 +344,11 @@ def topk_accumulate(values, indices, m: int, n: int, bucket: int, k: int, acc=No
 
 
 # -------------------------------------------------- bucketing front-end
-# [GCQC, "When it breaks": compression is per-tensor and small tensors
-# dominate the launch cost; bucketing many small tensors into one buffer is
-# what makes the exchange efficient.]  Reading: the tensors are
-# concatenated in list order into one buffer, which is then encoded (or
-# decoded and split back) exactly as a single buffer is.
+# [GCQC, "When it breaks".]  The page's remedy for per-tensor overhead is
+# to gather a model's many gradient tensors into one bucketed buffer before
+# compressing.  Reading: the tensors are concatenated in list order into one
+# buffer, which is then encoded (or decoded and split back) exactly as a
+# single buffer is.
 
 
 def concat(tensors):

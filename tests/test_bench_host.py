@@ -71,3 +71,9 @@ def test_counter_traffic_is_dropped_when_a_kernel_changes(bench, monkeypatch):
             e["hbm_bytes"] - e["fetch_bytes"] - e["write_bytes"]) <= 1, op
     monkeypatch.setattr(bench, "source_hash", lambda op: "0" * 16)
     assert all(bench.load_traffic(op) is None for op in t["ops"])
+
+
+def test_host_cpu_is_reported(bench):
+    n, model = bench.host_cpu()
+    assert isinstance(n, int) and n >= 1
+    assert isinstance(model, str) and model

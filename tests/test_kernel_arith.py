@@ -10,7 +10,11 @@ claimed to give exactly the result of the plain formula:
   fl(x * r) with r within an ulp of 1/scale, except where that product lies
   within 8 ulps of an E4M3 rounding point or below 2^-6 (checked here on
   crafted quotients that straddle every rounding point, with r one ulp off
-  either way, against the code of the true quotient).
+  either way, against the code of the true quotient), and with r computed
+  exactly as the kernel computes it: one Newton step
+  fma(fma(-sc, r0, 1), r0, r0) on a hardware reciprocal r0 that is fl(1/sc)
+  or one of its neighbours (its documented accuracy), the two fmas
+  evaluated in exact rational arithmetic and rounded once each.
 
 Both are the formulas as the kernels write them, evaluated with IEEE fp32
 arithmetic on the host (numpy float32; C fmaf)."""
@@ -182,3 +186,75 @@ def test_fp8_reciprocal_path_differs_from_division_in_the_quotient(ora):
     assert (q != y).sum() > 1000
     got, _ = fast_code(ora, x, sc)
     assert np.array_equal(got, ora.e4m3_from_f32_n(np.clip(y, np.float32(-448), np.float32(448))))
+
+
+def f32_rne(q):
+    """A rational rounded to the nearest fp32 (ties to even); normal range."""
+    from fractions import Fraction
+
+    q = Fraction(q)
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127
+    scaled = a / Fraction(2) ** (e - 23)  # in [2^23, 2^24)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return np.float32(sign * float(Fraction(m) * Fraction(2) ** (e - 23)))
+
+
+def kernel_reciprocal(sc, r0):
+    """The encoder's r: one Newton step on a hardware reciprocal r0,
+    fma(fma(-sc, r0, 1), r0, r0), each fma rounded once."""
+    from fractions import Fraction
+
+    s, q = Fraction(float(sc)), Fraction(float(r0))
+    e = f32_rne(1 - s * q)
+    return f32_rne(Fraction(float(e)) * q + q)
+
+
+def test_fp8_kernel_reciprocal_is_inside_the_tested_window(ora):
+    """The r the kernel really uses: the hardware reciprocal is accurate to
+    1 ulp, so r0 is fl(1/sc) or a neighbour; after the Newton step r must
+    lie within one ulp of fl(1/sc) (the window the tests above cover), and
+    the codes it gives must equal those of the division, on quotients
+    placed around every E4M3 rounding point."""
+    rng = np.random.default_rng(23)
+    mids = e4m3_midpoints()
+    for trial in range(300):
+        amax = np.float32(np.ldexp(rng.uniform(1, 2), int(rng.integers(-100, 100))))
+        sc = np.float32(amax / np.float32(448))
+        ref = np.float32(1.0) / sc
+        ulp_window = {ref, np.nextafter(ref, np.float32(np.inf)), np.nextafter(ref, np.float32(0))}
+        t = (mids.astype(np.float64) * np.float64(sc)).astype(np.float32)
+        k = rng.integers(-12, 13, t.size)
+        x = t.copy()
+        for _ in range(12):
+            step = np.abs(k) > _
+            x = np.where(step, np.nextafter(x, np.where(k >= 0, np.inf, -np.inf).astype(np.float32)), x)
+        x = np.concatenate([x, -x, rng.uniform(-1, 1, 2048).astype(np.float32) * amax]).astype(np.float32)
+        want = ora.e4m3_from_f32_n(np.clip((x / sc).astype(np.float32), np.float32(-448), np.float32(448)))
+        for r0 in (ref, np.nextafter(ref, np.float32(np.inf)), np.nextafter(ref, np.float32(0))):
+            r = kernel_reciprocal(sc, r0)
+            assert r in ulp_window, (trial, float(sc), float(r0), float(r))
+            got, _ = fast_code(ora, x, sc, r)
+            assert np.array_equal(got, want), trial
+
+
+def test_f32_rne_rounds_ties_to_even():
+    from fractions import Fraction
+
+    one = Fraction(1)
+    ulp = Fraction(1, 2 ** 23)
+    assert f32_rne(one + ulp / 2) == np.float32(1.0)          # tie, even stays
+    assert f32_rne(one + ulp + ulp / 2) == np.float32(1.0) + np.float32(2.0 ** -22)  # tie, odd rounds up
+    assert f32_rne(one + ulp / 2 + Fraction(1, 2 ** 60)) == np.nextafter(np.float32(1), np.float32(2))
+    assert f32_rne(Fraction(1, 3)) == np.float32(1) / np.float32(3)

@@ -300,7 +300,8 @@ def test_uniform_error_feedback_invariants(ora, bits):
     """[QCD "Error Feedback for Quantization"; GCQC "Error feedback ..."]:
     per step e_new + DQ = e_old + g up to two roundings, and over steps the
     sum of what was sent plus the final residual equals the sum of the
-    gradients (nothing is lost, only delayed)."""
+    gradients: a quantization error is carried into the next step rather
+    than dropped."""
     n, B = 65536, 4096
     ef = np.zeros(n, np.float32)
     sent = np.zeros(n, np.float64)

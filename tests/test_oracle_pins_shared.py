@@ -147,7 +147,7 @@ def test_int8_shared_error_bound_and_feedback(ora):
         sent += dq32
         gsum += g
         bound += step_bound
-    # nothing is lost, only delayed: the roundings of each step are all
+    # the error is carried forward, not dropped: the roundings of each step are all
     assert np.all(np.abs(sent + ef - gsum) <= bound * (1 + 1e-9))
 
 
