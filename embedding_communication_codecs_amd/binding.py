@@ -30,6 +30,8 @@ EXPORTS = (
     "qc_encode_qsgd",
     "qc_encode_ternary", "qc_encode_sign", "qc_bucket_absmax", "qc_absmax_combine", "qc_encode_int8_shared",
     "qc_sum_int8_shared", "qc_tensor_index", "qc_encode_topk", "qc_decode_topk", "qc_topk_accumulate",
+    "qc_encode_uniform_stochastic_multi", "qc_encode_qsgd_multi", "qc_encode_ternary_multi", "qc_encode_sign_multi",
+    "qc_bucket_absmax_multi", "qc_encode_int8_shared_multi",
     "qc_decode", "qc_decode_multi", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
@@ -61,6 +63,12 @@ def lib() -> ctypes.CDLL:
             "qc_decode_topk": [P, P, I64, I32, I32, P, P],
             "qc_topk_accumulate": [P, P, I32, I64, I32, I32, P, I32, P],
             "qc_encode_uniform_multi": [P, P, P, I32, I64, P, I32, I32, P, P, P, P],
+            "qc_encode_uniform_stochastic_multi": [P, P, P, I32, I64, P, I32, I32, U64, U64, P, P, P, P],
+            "qc_encode_qsgd_multi": [P, P, P, I32, I64, P, I32, I32, U64, U64, P, P, P],
+            "qc_encode_ternary_multi": [P, P, P, I32, I64, P, I32, U64, U64, P, P, P],
+            "qc_encode_sign_multi": [P, I32, P, P, I32, I64, P, I32, P, P, P],
+            "qc_bucket_absmax_multi": [P, P, P, I32, I64, P, I32, P, P],
+            "qc_encode_int8_shared_multi": [P, P, P, I32, I64, P, I32, P, P, P, P],
             "qc_decode_multi": [I32, P, P, P, I64, I32, I32, P, P, P, I32, P],
             "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
             "qc_encode_qsgd": [P, P, I64, I32, I32, U64, U64, P, P, P],
@@ -163,23 +171,27 @@ def qc_encode_ternary(x, ef, n, bucket, seed, elem_offset, words, scale, stream=
 
 
 class TensorTable:
-    """Device tables describing a list of fp32 GPU tensors as one buffer:
-    `xs` (int64 data pointers), and the bucket plan qc_tensor_index builds
-    on the host, `offsets` (prefix sums of the sizes, length ntensors + 1)
-    and `seg_first`.  Build it once per list layout and reuse it; it keeps
-    the tensors alive."""
+    """Device tables describing a list of GPU tensors of one dtype (float32,
+    or bfloat16 for the sign encoder) as one buffer: `xs` (int64 data
+    pointers), and the bucket plan qc_tensor_index builds on the host,
+    `offsets` (prefix sums of the sizes, length ntensors + 1) and
+    `seg_first`.  Build it once per list layout and reuse it; it keeps the
+    tensors alive."""
 
     def __init__(self, tensors):
         import torch
 
         if not tensors:
             raise ValueError("empty tensor list")
+        self.dtype = tensors[0].dtype
+        if self.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("tensors must be float32 or bfloat16")
         sizes = []
         for k, t in enumerate(tensors):
-            if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-                raise ValueError(f"tensor {k} must be a contiguous float32 GPU tensor")
-            if t.data_ptr() % 4:
-                raise ValueError(f"tensor {k} is not 4-byte aligned")
+            if not t.is_cuda or t.dtype != self.dtype or not t.is_contiguous():
+                raise ValueError(f"tensor {k} must be a contiguous {self.dtype} GPU tensor like tensor 0")
+            if t.data_ptr() % t.element_size():
+                raise ValueError(f"tensor {k} is not aligned to its element size")
             sizes.append(t.numel())
         import numpy as np
 
@@ -216,6 +228,63 @@ def qc_encode_uniform_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, bit
         _ptr(xs, 8 * max(ntensors, 0), "xs"), _ptr(offsets, 8 * (max(ntensors, 0) + 1), "offsets"),
         _ptr(seg_first, 4 * _nseg(n), "seg_first"), ntensors, n, _ptr(ef, 4 * n, "ef"), bucket, bits,
         _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"), _ptr(zero, 4 * nb, "zero"), _stream(stream)))
+
+
+def _list_args(xs, offsets, seg_first, ntensors, n):
+    return (_ptr(xs, 8 * max(ntensors, 0), "xs"), _ptr(offsets, 8 * (max(ntensors, 0) + 1), "offsets"),
+            _ptr(seg_first, 4 * _nseg(n), "seg_first"), ntensors, n)
+
+
+def qc_encode_uniform_stochastic_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, seed, elem_offset,
+                                       codes, scale, zero, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_UNIFORM, n, bucket, bits) if bits in UNIFORM_BITS and n >= 0 else None
+    _check(lib().qc_encode_uniform_stochastic_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, bits,
+        seed & (2**64 - 1), elem_offset, _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"),
+        _ptr(zero, 4 * nb, "zero"), _stream(stream)))
+
+
+def qc_encode_qsgd_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, levels, seed, elem_offset, words, norm,
+                         stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_QSGD, n, bucket, 16) if n >= 0 else None
+    _check(lib().qc_encode_qsgd_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, levels,
+        seed & (2**64 - 1), elem_offset, _ptr(words, pb, "words"), _ptr(norm, 4 * nb, "norm"), _stream(stream)))
+
+
+def qc_encode_ternary_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, seed, elem_offset, words, scale,
+                            stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_TERNARY, n, bucket, 2) if n >= 0 else None
+    _check(lib().qc_encode_ternary_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, seed & (2**64 - 1),
+        elem_offset, _ptr(words, pb, "words"), _ptr(scale, 4 * nb, "scale"), _stream(stream)))
+
+
+def qc_encode_sign_multi(xs, xtype, offsets, seg_first, ntensors, n, ef, bucket, words, scale, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_SIGN, n, bucket, 1) if n >= 0 else None
+    a = _list_args(xs, offsets, seg_first, ntensors, n)
+    _check(lib().qc_encode_sign_multi(
+        a[0], xtype, *a[1:], _ptr(ef, 4 * n, "ef"), bucket, _ptr(words, pb, "words"), _ptr(scale, 4 * nb, "scale"),
+        _stream(stream)))
+
+
+def qc_bucket_absmax_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, amax, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    _check(lib().qc_bucket_absmax_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, _ptr(amax, 4 * nb, "amax"),
+        _stream(stream)))
+
+
+def qc_encode_int8_shared_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, amax, codes, scale, stream=None):
+    nb = nbuckets(n, bucket) if n > 0 and bucket > 0 else 0
+    pb = payload_bytes(QC_INT8_SHARED, n, bucket, 8) if n >= 0 else None
+    _check(lib().qc_encode_int8_shared_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, _ptr(amax, 4 * nb, "amax"),
+        _ptr(codes, pb, "codes"), _ptr(scale, 4 * nb, "scale"), _stream(stream)))
 
 
 def qc_encode_fp8_rowwise(x, rows, dim, codes, scale, stream=None):

@@ -229,13 +229,15 @@ __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ codes, in
     }
 }
 
+// Tile bk of G::B elements, inside statistics group gb of ng groups (a tile
+// is the whole group, or a part of it for the largest groups).
 template <class G, int F, int RQBITS, bool RQ, bool FULL>
 __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-                                           const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb,
+                                           const float* __restrict__ zero, int32_t m, int64_t n, int64_t ng,
                                            int64_t pbytes, float* __restrict__ acc, int32_t accumulate,
                                            uint8_t* __restrict__ rq_codes, int64_t rq_pbytes,
                                            float* __restrict__ rq_scale, float* __restrict__ rq_zero,
-                                           int64_t bk, float* lds) {
+                                           int64_t bk, int64_t gb, float* lds) {
     constexpr int K = G::K, LPB = G::LPB, UW = 2;
     const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
 
@@ -279,7 +281,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
     Stats<G, F> st;
     auto add_worker = [&](int32_t w, const ChunkBits<F> (&c)[K]) {
         float s, z;
-        st.get(scale, zero, nb, bk, w, s, z);
+        st.get(scale, zero, ng, gb, w, s, z);
         if constexpr (F == A_QSGD) z = s / 7.0f;
         if (needs_exact_path<F>(s, z)) {
             if constexpr (F == A_QSGD || F == A_TER) {
@@ -294,7 +296,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
     for (int32_t c0 = 0; c0 < m; c0 += CHUNK) {
         const int32_t cend = m - c0 > CHUNK ? c0 + CHUNK : m;
         const int32_t last = cend - 1;
-        st.load_chunk_of_workers(scale, zero, nb, bk, c0, cend);
+        st.load_chunk_of_workers(scale, zero, ng, gb, c0, cend);
         ChunkBits<F> slot[UW][K];
 #pragma unroll
         for (int u = 0; u < UW; ++u)
@@ -399,11 +401,14 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
     }
 }
 
+// nb tiles of G::B elements; tile bk belongs to statistics group
+// bk >> tshift of ng (tshift = 0 when a tile is a whole group, which
+// requantization requires).
 template <class G, int F, int RQBITS, bool RQ>
 __global__ void __launch_bounds__(G::THREADS)
 k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-              const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb, int64_t pbytes,
-              float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,
+              const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb, int64_t ng, int32_t tshift,
+              int64_t pbytes, float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,
               int64_t rq_pbytes, float* __restrict__ rq_scale, float* __restrict__ rq_zero) {
     __shared__ float lds[G::W];
 
@@ -421,18 +426,23 @@ k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale
         // a bucket spanning whole waves has a wave-uniform index: keep it in
         // scalar registers so per-worker statistics come through the scalar cache
         if constexpr (G::LPB == WAVE) bks = __builtin_amdgcn_readfirstlane((int)bk);
+        const int64_t gb = bks >> tshift;
         if ((bks + 1) * (int64_t)G::B <= n)
-            acc_bucket<G, F, RQBITS, RQ, true>(codes, scale, zero, m, n, nb, pbytes, acc, accumulate,
-                                               rq_codes, rq_pbytes, rq_scale, rq_zero, bks, lds);
+            acc_bucket<G, F, RQBITS, RQ, true>(codes, scale, zero, m, n, ng, pbytes, acc, accumulate,
+                                               rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds);
         else
-            acc_bucket<G, F, RQBITS, RQ, false>(codes, scale, zero, m, n, nb, pbytes, acc, accumulate,
-                                                rq_codes, rq_pbytes, rq_scale, rq_zero, bks, lds);
+            acc_bucket<G, F, RQBITS, RQ, false>(codes, scale, zero, m, n, ng, pbytes, acc, accumulate,
+                                                rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds);
     }
 }
 
 // Bucket of `group` elements as LPB lanes x K chunks of 16 x W waves: whole
 // waves with up to 4 chunks per lane before spreading over more waves.
-template <class Fn>
+// 65,536-element groups (and FP8 rows of 32,768) are summed in tiles of
+// 16,384 elements, each reading its group's statistics: holding a whole
+// group, those kernels spilled to scratch memory (64 sums per lane in a
+// 1,024-thread block; FP8's decode on top of 64 sums in a 512-thread one).
+template <int F, class Fn>
 hipError_t dispatch_group(int32_t group, Fn&& fn) {
     switch (group / 16) {
         case 4: return fn(Geom<16, 4, 1, 1>{});
@@ -444,34 +454,56 @@ hipError_t dispatch_group(int32_t group, Fn&& fn) {
         case 256: return fn(Geom<16, 64, 4, 1>{});
         case 512: return fn(Geom<16, 64, 4, 2>{});
         case 1024: return fn(Geom<16, 64, 4, 4>{});
-        case 2048: return fn(Geom<16, 64, 4, 8>{});
-        case 4096: return fn(Geom<16, 64, 4, 16>{});
+        case 2048:
+            if constexpr (F == A_FP8) return fn(Geom<16, 64, 4, 4>{});
+            else return fn(Geom<16, 64, 4, 8>{});
+        case 4096: return fn(Geom<16, 64, 4, 4>{});
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_encode_requant(const float* acc, int64_t n, int32_t group, int32_t bits, void* rq_codes,
+                                 float* rq_scale, float* rq_zero, hipStream_t stream) {
+    const int64_t code_bytes = bits == 8 ? n : (bits == 4 ? (n + 7) / 8 * 4 : (n + 15) / 16 * 4);
+    return launch_encode_uniform(acc, nullptr, n, group, bits, false, 0, 0, rq_codes, (code_bytes + 15) / 16 * 16,
+                                 rq_scale, rq_zero, stream);
 }
 
 template <int F>
 hipError_t launch_fmt(const void* codes, const float* scale, const float* zero, int32_t m, int64_t n,
                       int32_t group, int32_t bits, int64_t pbytes, float* acc, bool accumulate,
                       void* rq_codes, float* rq_scale, float* rq_zero, hipStream_t stream) {
-    const int64_t nb = (n + group - 1) / group;
-    return dispatch_group(group, [&](auto g) {
+    const int64_t ng = (n + group - 1) / group;
+    return dispatch_group<F>(group, [&](auto g) {
         using G = decltype(g);
-        int64_t blocks = grid_for(nb, G::BPB);
+        const int32_t tshift = log2_exact(group / G::B);
+        const int64_t nt = (n + G::B - 1) / G::B;
+        int64_t blocks = grid_for(nt, G::BPB);
         blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
         const dim3 grid((unsigned)blocks), block(G::THREADS);
         const int64_t rq_code_bytes = bits == 8 ? n : (bits == 4 ? (n + 7) / 8 * 4 : (n + 15) / 16 * 4);
         const int64_t rq_pbytes = (rq_code_bytes + 15) / 16 * 16;
-        if (rq_codes == nullptr) {
+        if (rq_codes == nullptr || tshift > 0) {
             hipLaunchKernelGGL((k_dequant_acc<G, F, 8, false>), grid, block, 0, stream,
-                               (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                               (const uint8_t*)codes, scale, zero, m, n, nt, ng, tshift, pbytes, acc,
                                (int32_t)accumulate, (uint8_t*)nullptr, (int64_t)0, (float*)nullptr,
                                (float*)nullptr);
+            if (rq_codes == nullptr) return hipGetLastError();
+            if constexpr (F == A_U8 || F == A_U4 || F == A_U2) {
+                // tiles smaller than the group: the sums are requantized by
+                // the uniform encoder in a second launch (the same rule,
+                // without error feedback), reading them back once
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                return launch_encode_requant(acc, n, group, bits, rq_codes, rq_scale, rq_zero, stream);
+            } else {
+                return hipErrorInvalidValue;
+            }
         } else if constexpr (F == A_U8 || F == A_U4 || F == A_U2) {
             // requantization to the input's own bit width
             constexpr int RQB = F == A_U8 ? 8 : (F == A_U4 ? 4 : 2);
             hipLaunchKernelGGL((k_dequant_acc<G, F, RQB, true>), grid, block, 0, stream,
-                               (const uint8_t*)codes, scale, zero, m, n, nb, pbytes, acc,
+                               (const uint8_t*)codes, scale, zero, m, n, nt, ng, tshift, pbytes, acc,
                                (int32_t)accumulate, (uint8_t*)rq_codes, rq_pbytes, rq_scale, rq_zero);
         } else {
             return hipErrorInvalidValue;

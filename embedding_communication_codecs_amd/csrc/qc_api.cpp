@@ -31,6 +31,11 @@ hipStream_t hs(qc_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 // Bucket indices are handled as 32-bit values inside some kernels.
 constexpr int64_t kMaxBuckets = (int64_t(1) << 31) - 1;
 
+// Largest concatenation a tensor list may describe: far beyond any device
+// memory, and small enough that the prefix sums and the per-segment index
+// cannot overflow.
+constexpr int64_t kMaxListElems = int64_t(1) << 56;
+
 }  // namespace
 
 extern "C" {
@@ -100,12 +105,14 @@ int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t b
 
 int qc_tensor_index(const int64_t* sizes, int32_t ntensors, int64_t* offsets, int32_t* seg_first) {
     if (!sizes || !offsets || !seg_first || ntensors < 1) return QC_ERR_ARG;
-    offsets[0] = 0;
+    // every size is checked, and the total bounded, before anything is written
+    int64_t n = 0;
     for (int32_t t = 0; t < ntensors; ++t) {
-        if (sizes[t] < 0) return QC_ERR_ARG;
-        offsets[t + 1] = offsets[t] + sizes[t];
+        if (sizes[t] < 0 || sizes[t] > kMaxListElems - n) return QC_ERR_ARG;
+        n += sizes[t];
     }
-    const int64_t n = offsets[ntensors];
+    offsets[0] = 0;
+    for (int32_t t = 0; t < ntensors; ++t) offsets[t + 1] = offsets[t] + sizes[t];
     const int64_t nseg = (n + (int64_t(1) << QC_INDEX_SHIFT) - 1) >> QC_INDEX_SHIFT;
     int32_t t = 0;
     for (int64_t j = 0; j <= nseg; ++j) {
@@ -119,21 +126,118 @@ int qc_tensor_index(const int64_t* sizes, int32_t ntensors, int64_t* offsets, in
     return QC_OK;
 }
 
+namespace {
+
+// Checks shared by the *_multi encoders: the list tables (validated as far as
+// the host can: pointers present and aligned), the bucket, and n.  Returns
+// QC_OK with `l` filled, or the error status.
+int check_list(const void* const* xs, const int64_t* offsets, const int32_t* seg_first, int32_t ntensors,
+               int64_t n, int32_t bucket, qc::ListSrc& l) {
+    if (n < 0 || ntensors < 1 || bad_bucket(bucket)) return QC_ERR_ARG;
+    if (bucket > QC_MAX_LIST_BUCKET) return QC_ERR_UNSUPPORTED;
+    if (n == 0) return QC_OK;  // an empty call: the caller returns before using l
+    if (!xs || !offsets || !seg_first) return QC_ERR_ARG;
+    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
+    if (misaligned8(xs) || misaligned8(offsets) || misaligned4(seg_first)) return QC_ERR_ALIGN;
+    l = qc::ListSrc{xs, offsets, seg_first, ntensors, n};
+    return QC_OK;
+}
+
+int encode_uniform_list(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                        int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits, bool stochastic,
+                        uint64_t seed, uint64_t elem_offset, void* codes, float* scale, float* zero,
+                        qc_stream_t stream) {
+    qc::ListSrc l;
+    int st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l);
+    if (st == QC_OK && (elem_offset & 3u) != 0) st = QC_ERR_ARG;
+    if (st == QC_OK && bits != 8 && bits != 4 && bits != 2) st = QC_ERR_UNSUPPORTED;
+    if (st != QC_OK || n == 0) return st;
+    if (!codes || !scale || !zero) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(codes) || misaligned(scale) || misaligned(zero)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_uniform_list(l, ef, bucket, bits, stochastic, seed, elem_offset, codes,
+                                                   qc_payload_bytes(QC_UNIFORM, n, bucket, bits), scale, zero,
+                                                   hs(stream)));
+}
+
+}  // namespace
+
 int qc_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
                             int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits, void* codes,
                             float* scale, float* zero, qc_stream_t stream) {
-    if (n < 0 || ntensors < 1 || bad_bucket(bucket)) return QC_ERR_ARG;
-    if (bits != 8 && bits != 4 && bits != 2) return QC_ERR_UNSUPPORTED;
-    if (bucket > QC_MAX_LIST_BUCKET) return QC_ERR_UNSUPPORTED;
-    if (n == 0) return QC_OK;
-    if (!xs || !offsets || !seg_first || !codes || !scale || !zero) return QC_ERR_ARG;
-    if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
-    if (misaligned8(xs) || misaligned8(offsets) || misaligned4(seg_first) || misaligned(ef) || misaligned(codes) ||
-        misaligned(scale) || misaligned(zero))
-        return QC_ERR_ALIGN;
-    return launched(qc::launch_encode_uniform_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, false, 0,
-                                                    0, codes, qc_payload_bytes(QC_UNIFORM, n, bucket, bits), scale,
-                                                    zero, hs(stream)));
+    return encode_uniform_list(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, false, 0, 0, codes, scale,
+                               zero, stream);
+}
+
+int qc_encode_uniform_stochastic_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                       int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
+                                       uint64_t seed, uint64_t elem_offset, void* codes, float* scale, float* zero,
+                                       qc_stream_t stream) {
+    return encode_uniform_list(xs, offsets, seg_first, ntensors, n, ef, bucket, bits, true, seed, elem_offset,
+                               codes, scale, zero, stream);
+}
+
+int qc_encode_qsgd_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t levels, uint64_t seed,
+                         uint64_t elem_offset, uint32_t* words, float* norm, qc_stream_t stream) {
+    qc::ListSrc l;
+    int st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l);
+    if (st == QC_OK && (elem_offset & 3u) != 0) st = QC_ERR_ARG;
+    if (st == QC_OK && levels != 16) st = QC_ERR_UNSUPPORTED;
+    if (st != QC_OK || n == 0) return st;
+    if (!words || !norm) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(words) || misaligned(norm)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_qsgd_list(l, ef, bucket, seed, elem_offset, words,
+                                                qc_payload_bytes(QC_QSGD, n, bucket, 16), norm, hs(stream)));
+}
+
+int qc_encode_ternary_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                            int32_t ntensors, int64_t n, float* ef, int32_t bucket, uint64_t seed,
+                            uint64_t elem_offset, uint32_t* words, float* scale, qc_stream_t stream) {
+    qc::ListSrc l;
+    int st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l);
+    if (st == QC_OK && (elem_offset & 3u) != 0) st = QC_ERR_ARG;
+    if (st != QC_OK || n == 0) return st;
+    if (!words || !scale) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(words) || misaligned(scale)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_ternary_list(l, ef, bucket, seed, elem_offset, words,
+                                                   qc_payload_bytes(QC_TERNARY, n, bucket, 2), scale, hs(stream)));
+}
+
+int qc_encode_sign_multi(const void* const* xs, int32_t xtype, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, uint32_t* words, float* scale,
+                         qc_stream_t stream) {
+    qc::ListSrc l;
+    int st = check_list(xs, offsets, seg_first, ntensors, n, bucket, l);
+    if (st == QC_OK && xtype != QC_F32 && xtype != QC_BF16) st = QC_ERR_ARG;
+    if (st != QC_OK || n == 0) return st;
+    if (!words || !scale) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(words) || misaligned(scale)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_sign_list(l, xtype == QC_BF16, ef, bucket, words,
+                                                qc_payload_bytes(QC_SIGN, n, bucket, 1), scale, hs(stream)));
+}
+
+int qc_bucket_absmax_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                           int32_t ntensors, int64_t n, const float* ef, int32_t bucket, float* amax,
+                           qc_stream_t stream) {
+    qc::ListSrc l;
+    const int st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l);
+    if (st != QC_OK || n == 0) return st;
+    if (!amax) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(amax)) return QC_ERR_ALIGN;
+    return launched(qc::launch_bucket_absmax_list(l, ef, bucket, amax, hs(stream)));
+}
+
+int qc_encode_int8_shared_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                int32_t ntensors, int64_t n, float* ef, int32_t bucket, const float* amax,
+                                uint8_t* codes, float* scale, qc_stream_t stream) {
+    qc::ListSrc l;
+    const int st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l);
+    if (st != QC_OK || n == 0) return st;
+    if (!amax || !codes || !scale) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned(amax) || misaligned(codes) || misaligned(scale)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_int8_shared_list(l, ef, bucket, amax, codes,
+                                                       qc_payload_bytes(QC_INT8_SHARED, n, bucket, 8), scale,
+                                                       hs(stream)));
 }
 
 int qc_encode_fp8_rowwise(const float* x, int64_t rows, int32_t dim, uint8_t* codes, float* scale,

@@ -22,10 +22,39 @@ hipError_t launch_encode_uniform(const float* x, float* ef, int64_t n, int32_t b
                                  bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
                                  int64_t payload_bytes, float* scale, float* zero, hipStream_t stream);
 
-hipError_t launch_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
-                                       int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
-                                       bool stochastic, uint64_t seed, uint64_t elem_offset, void* codes,
-                                       int64_t payload_bytes, float* scale, float* zero, hipStream_t stream);
+// A list of tensors read in place as one concatenated input: the device
+// table of their pointers, the device copies of the prefix offsets and the
+// per-segment index built by qc_tensor_index, and the total element count.
+struct ListSrc {
+    const void* const* xs;
+    const int64_t* offsets;
+    const int32_t* seg_first;
+    int32_t ntensors;
+    int64_t n;
+};
+
+hipError_t launch_encode_uniform_list(const ListSrc& l, float* ef, int32_t bucket, int32_t bits, bool stochastic,
+                                      uint64_t seed, uint64_t elem_offset, void* codes, int64_t payload_bytes,
+                                      float* scale, float* zero, hipStream_t stream);
+
+hipError_t launch_encode_ternary_list(const ListSrc& l, float* ef, int32_t bucket, uint64_t seed,
+                                      uint64_t elem_offset, uint32_t* words, int64_t payload_bytes, float* scale,
+                                      hipStream_t stream);
+
+hipError_t launch_encode_qsgd_list(const ListSrc& l, float* ef, int32_t bucket, uint64_t seed, uint64_t elem_offset,
+                                   uint32_t* words, int64_t payload_bytes, float* norm, hipStream_t stream);
+
+hipError_t launch_encode_sign_list(const ListSrc& l, bool bf16, float* ef, int32_t bucket, uint32_t* words,
+                                   int64_t payload_bytes, float* scale, hipStream_t stream);
+
+hipError_t launch_bucket_absmax_list(const ListSrc& l, const float* ef, int32_t bucket, float* amax,
+                                     hipStream_t stream);
+
+hipError_t launch_encode_int8_shared_list(const ListSrc& l, float* ef, int32_t bucket, const float* amax,
+                                          uint8_t* codes, int64_t payload_bytes, float* scale, hipStream_t stream);
+
+hipError_t launch_encode_topk_list(const ListSrc& l, float* ef, int32_t bucket, int32_t k, float* values,
+                                   uint32_t* indices, hipStream_t stream);
 
 hipError_t launch_encode_ternary(const float* x, float* ef, int64_t n, int32_t bucket, uint64_t seed,
                                  uint64_t elem_offset, uint32_t* words, int64_t payload_bytes,

@@ -118,9 +118,11 @@ int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t b
 
 /*
  * Bucketing front-end ("Gradient Compression and Quantised Collectives",
- * section "When it breaks": compression is per-tensor and small tensors
- * dominate the launch cost; bucketing many small tensors into one buffer is
- * what makes the exchange efficient).  Encodes the concatenation of a list
+ * section "When it breaks").  A model's gradient arrives as hundreds of
+ * tensors, many of them tiny; one launch per tensor costs more in launch
+ * overhead and short buckets than the codec itself.  This call takes the
+ * whole list at once and reads each tensor where it lies, with no copy into
+ * a staging buffer first.  Encodes the concatenation of a list
  * of fp32 tensors, in list order, exactly as qc_encode_uniform encodes that
  * concatenation held in one buffer, in one launch and without copying the
  * tensors: buckets run across tensor boundaries; ef, codes, scale and zero
@@ -151,17 +153,66 @@ int qc_encode_uniform_stochastic(const float* x, float* ef, int64_t n, int32_t b
  *                          n - 1), i.e. the last t with offsets[t] at or
  *                          below it (0 when n == 0).
  * The caller copies both to the device for the *_multi calls.
- * Returns QC_OK, or QC_ERR_ARG for NULL arrays, ntensors < 1 or a negative
- * size.
+ * Returns QC_OK, or QC_ERR_ARG for NULL arrays, ntensors < 1, a negative
+ * size or a total above 2^56 elements; every size is checked before
+ * anything is written, so a rejected call leaves offsets and seg_first
+ * untouched.
  */
 #define QC_INDEX_SHIFT 12
-/* Largest bucket qc_encode_uniform_multi accepts. */
+/*
+ * Largest bucket the *_multi encoders accept.  At 65,536 the tensor-list
+ * kernels need more registers than a lane has and would spill to scratch
+ * memory; no kernel of this library uses scratch memory (spilled builds of
+ * the flat 65,536-element encoders gave results that differ from their
+ * source's), so that one size is left to the flat encoders.
+ */
 #define QC_MAX_LIST_BUCKET 32768
 int qc_tensor_index(const int64_t* sizes, int32_t ntensors, int64_t* offsets, int32_t* seg_first);
 
 int qc_encode_uniform_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
                             int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits, void* codes,
                             float* scale, float* zero, qc_stream_t stream);
+
+/*
+ * The other encoders over a tensor list, each encoding the concatenation of
+ * the list exactly as its flat form (named below) encodes that
+ * concatenation held in one buffer, in one launch, reading the tensors in
+ * place ("Gradient Compression and Quantised Collectives", section "When it
+ * breaks").  xs, offsets, seg_first, ntensors and n are as for
+ * qc_encode_uniform_multi; every other argument, the results and the
+ * errors are those of the flat form, plus the list errors of
+ * qc_encode_uniform_multi (ALIGN for the tables, UNSUPPORTED for buckets
+ * above QC_MAX_LIST_BUCKET).  Stochastic codecs draw for global element
+ * elem_offset + (index in the concatenation).
+ *
+ *   qc_encode_uniform_stochastic_multi   qc_encode_uniform_stochastic
+ *   qc_encode_qsgd_multi                 qc_encode_qsgd
+ *   qc_encode_ternary_multi              qc_encode_ternary
+ *   qc_encode_sign_multi                 qc_encode_sign: xs are fp32 or bf16
+ *                                        tensors (xtype), any 4- or 2-byte
+ *                                        alignment
+ *   qc_bucket_absmax_multi               qc_bucket_absmax
+ *   qc_encode_int8_shared_multi          qc_encode_int8_shared
+ */
+int qc_encode_uniform_stochastic_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                       int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
+                                       uint64_t seed, uint64_t elem_offset, void* codes, float* scale, float* zero,
+                                       qc_stream_t stream);
+int qc_encode_qsgd_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t levels, uint64_t seed,
+                         uint64_t elem_offset, uint32_t* words, float* norm, qc_stream_t stream);
+int qc_encode_ternary_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                            int32_t ntensors, int64_t n, float* ef, int32_t bucket, uint64_t seed,
+                            uint64_t elem_offset, uint32_t* words, float* scale, qc_stream_t stream);
+int qc_encode_sign_multi(const void* const* xs, int32_t xtype, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, uint32_t* words, float* scale,
+                         qc_stream_t stream);
+int qc_bucket_absmax_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                           int32_t ntensors, int64_t n, const float* ef, int32_t bucket, float* amax,
+                           qc_stream_t stream);
+int qc_encode_int8_shared_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                                int32_t ntensors, int64_t n, float* ef, int32_t bucket, const float* amax,
+                                uint8_t* codes, float* scale, qc_stream_t stream);
 
 /*
  * Rowwise FP8 (OCP E4M3FN) for embedding-lookup payloads: one byte per
@@ -296,7 +347,8 @@ int qc_decode_multi(int32_t fmt, const void* codes, const float* scale, const fl
  * common rules).  If rq_codes is non-NULL the summed vector is then
  * requantized with qc_encode_uniform's rule (no error feedback, same
  * bits and bucket = group) into rq_codes/rq_scale/rq_zero, in the same
- * pass.
+ * pass (for group = 65,536, by a second kernel that reads the sums back
+ * once: the sums of such a group are formed in tiles).
  *
  *   fmt/group/bits as for qc_decode.  m in [1, QC_MAX_WORKERS].
  *   codes   m payloads, read.  scale/zero fp32[m * nb], read.

@@ -280,9 +280,14 @@ def test_tensor_index_plan(qc):
             if n > 0:
                 assert offs[seg[j]] <= g < offs[seg[j] + 1], (j, g, seg[j])
                 assert seg[j] == t
-    bad = np.array([3, -1], np.int64)
-    with pytest.raises(qc.QcError):
-        qc.qc_tensor_index(bad, 2, np.empty(3, np.int64), np.empty(2, np.int32))
+    # a rejected plan writes nothing: a negative size after a valid one, and
+    # sizes whose total would pass 2^56 elements
+    for bad in (np.array([3, -1], np.int64), np.array([5, 1 << 55, 1 << 55, 7], np.int64)):
+        offs = np.full(bad.size + 1, -77, np.int64)
+        seg = np.full(8, -77, np.int32)
+        with pytest.raises(qc.QcError):
+            qc.qc_tensor_index(bad, bad.size, offs, seg)
+        assert np.all(offs == -77) and np.all(seg == -77)
 
 
 def test_multi_entry_point_errors(qc):
@@ -317,6 +322,46 @@ def test_multi_entry_point_errors(qc):
     args = list(ok)
     args[9] = A + 2
     assert call(qc, f, *args) == qc.QC_ERR_ALIGN
+
+
+# The other encoders' list forms: (name, valid arguments, positions of
+# required pointers, position of the bucket, positions of 16-byte aligned
+# outputs).  The list tables sit at positions 0-2 (0, 2, 3 for sign).
+LIST_CALLS = [
+    ("qc_encode_uniform_stochastic_multi", (A, A, A, 5, 1000, A, 512, 4, 7, 0, A, A, A, None), (10, 11, 12), 6,
+     (5, 10)),
+    ("qc_encode_qsgd_multi", (A, A, A, 5, 1000, A, 512, 16, 7, 0, A, A, None), (10, 11), 6, (5, 10)),
+    ("qc_encode_ternary_multi", (A, A, A, 5, 1000, A, 512, 7, 0, A, A, None), (9, 10), 6, (5, 9)),
+    ("qc_encode_sign_multi", (A, 1, A, A, 5, 1000, A, 512, A, A, None), (8, 9), 7, (6, 8)),
+    ("qc_bucket_absmax_multi", (A, A, A, 5, 1000, A, 512, A, None), (7,), 6, (5, 7)),
+    ("qc_encode_int8_shared_multi", (A, A, A, 5, 1000, A, 512, A, A, A, None), (7, 8, 9), 6, (5, 8)),
+]
+
+
+@pytest.mark.parametrize("name,ok,required,bpos,aligned", LIST_CALLS, ids=[c[0] for c in LIST_CALLS])
+def test_list_encoders_errors(qc, name, ok, required, bpos, aligned):
+    tables = (0, 2, 3) if name == "qc_encode_sign_multi" else (0, 1, 2)
+    for pos in tables + required:
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, name, *args) == qc.QC_ERR_ARG, pos
+    for bucket, st in ((65536, qc.QC_ERR_UNSUPPORTED), (100, qc.QC_ERR_ARG), (32, qc.QC_ERR_ARG)):
+        args = list(ok)
+        args[bpos] = bucket
+        assert call(qc, name, *args) == st, bucket
+    for pos in aligned:
+        args = list(ok)
+        args[pos] = MIS
+        assert call(qc, name, *args) == qc.QC_ERR_ALIGN, pos
+    args = list(ok)
+    args[tables[0]] = A + 4  # the pointer table must be 8-byte aligned
+    assert call(qc, name, *args) == qc.QC_ERR_ALIGN
+    # an empty list call is valid and does nothing, whatever the pointers
+    args = list(ok)
+    args[bpos - 2] = 0
+    for pos in required:
+        args[pos] = NULL
+    assert call(qc, name, *args) == qc.QC_OK
 
 
 def test_topk_errors(qc):

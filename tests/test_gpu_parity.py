@@ -40,7 +40,7 @@ def run_uniform(qc, x, ef, bucket, bits):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536])
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536])
 def test_uniform_parity_ef_steps(qc, ora, bucket, bits):
     n = 3 * bucket + 37
     ef_h = np.zeros(n, np.float32)
@@ -227,7 +227,7 @@ def run_qsgd(qc, x, ef, bucket, seed, offset):
     return words, norm
 
 
-@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 65536])
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 16384, 32768, 65536])
 def test_qsgd_parity_ef_steps(qc, ora, bucket):
     n = 3 * bucket + 37
     ef_h = np.zeros(n, np.float32)
@@ -288,7 +288,7 @@ def run_sign(qc, x, ef, bucket):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 65536])
+@pytest.mark.parametrize("bucket", [64, 128, 256, 512, 1024, 4096, 8192, 16384, 32768, 65536])
 def test_sign_parity_ef_steps(qc, ora, bucket, dtype):
     n = 3 * bucket + 37
     ef_h = np.zeros(n, np.float32)
@@ -382,8 +382,8 @@ FMT = {"u8": (0, 8), "u4": (0, 4), "fp8": (1, 8), "qsgd": (2, 16), "sign": (3, 1
 ORA_FMT = {"u8": 0, "u4": 0, "fp8": 1, "qsgd": 2, "sign": 3}
 
 
-@pytest.mark.parametrize("fmt,group", [("u8", 64), ("u8", 2048), ("u8", 4096), ("u8", 8192),
-                                       ("u4", 256), ("u4", 2048), ("fp8", 128), ("fp8", 64),
+@pytest.mark.parametrize("fmt,group", [("u8", 64), ("u8", 2048), ("u8", 4096), ("u8", 8192), ("u8", 16384),
+                                       ("u8", 32768), ("u4", 256), ("u4", 2048), ("fp8", 128), ("fp8", 64),
                                        ("qsgd", 512), ("sign", 4096), ("sign", 64)])
 @pytest.mark.parametrize("m", [1, 3, 5, 16])
 def test_dequant_accumulate_parity(qc, ora, fmt, group, m):
@@ -409,7 +409,7 @@ def test_dequant_accumulate_parity(qc, ora, fmt, group, m):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-@pytest.mark.parametrize("group", [64, 512, 2048, 8192])
+@pytest.mark.parametrize("group", [64, 512, 2048, 8192, 16384, 32768])
 def test_dequant_accumulate_requant(qc, ora, group, bits):
     m, n = 6, 3 * group + 21
     fmt = "u8" if bits == 8 else "u4"

@@ -12,7 +12,7 @@ from gpu_util import Out, bits_equal, dev, dev_ef, first_diff, need_gpu, out_f32
 
 pytestmark = pytest.mark.gpu
 
-BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536]
+BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
 
 
 @pytest.fixture(scope="module")
