@@ -615,6 +615,9 @@ def main():
                     help="also run a 1 GiB device copy each step (counter calibration)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure plain copy/fill/read bandwidth and print it")
+    ap.add_argument("--no-alone", action="store_true",
+                    help="skip timing each op alone (profiled runs keep only the timed passes)")
+    ap.add_argument("--no-calibration", action="store_true", help="skip the copy/fill/read calibration")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -656,18 +659,21 @@ def main():
     if ext_names:
         ext_ms, ext = time_ops(torch, ops, ext_names, sizes, args.steps, args.warmup, None)
         print(f"[bench] extensions timed ({ext_ms:.3f} ms per pass)", file=sys.stderr, flush=True)
-    time_alone(torch, ops, names, sizes, per_op, args.steps)
-    if ext is not None:
-        time_alone(torch, ops, ext_names, sizes, ext, args.steps)
-    print("[bench] each op timed alone", file=sys.stderr, flush=True)
+    if not args.no_alone:
+        time_alone(torch, ops, names, sizes, per_op, args.steps)
+        if ext is not None:
+            time_alone(torch, ops, ext_names, sizes, ext, args.steps)
+        print("[bench] each op timed alone", file=sys.stderr, flush=True)
     total_in = sum(sizes[o][0] for o in names)
     dom = max(names, key=lambda o: per_op[o]["ms"])
     achieved = per_op[dom]["hbm_GBps"]
     traffic = load_traffic(dom)
     st.clear()
     torch.cuda.empty_cache()
-    cal = calibrate(torch)
-    print("[bench] calibration copy/fill/read timed", file=sys.stderr, flush=True)
+    cal = None
+    if not args.no_calibration:
+        cal = calibrate(torch)
+        print("[bench] calibration copy/fill/read timed", file=sys.stderr, flush=True)
     result = {
         "metric": "codec GB/s (fp32 in, encode+EF / decode+accum) and % of MI355X HBM peak",
         "value": round(total_in / (ms_per_step * 1e-3) / 1e9, 2),

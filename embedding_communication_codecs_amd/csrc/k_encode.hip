@@ -260,7 +260,7 @@ __device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, int64_
         if (i < pbytes) st_u32(codes + i, word);
     } else if constexpr (BITS == 4) {
         const uint32_t half = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12);
-        const uint32_t other = (uint32_t)__shfl_xor((int)half, 1, WAVE);
+        const uint32_t other = lane_xor1(half);
         if ((lane_id() & 1) == 0 && i / 2 < pbytes) st_u32(codes + i / 2, half | (other << 16));
     } else {
         const uint32_t byte = q[0] | (q[1] << 2) | (q[2] << 4) | (q[3] << 6);
