@@ -83,7 +83,7 @@ def tensor_list_sizes():
 # traffic taken for an op stays valid while these files are unchanged.
 SHARED_SOURCES = ["qc_device.hpp", "qc_bucket.hpp", "qc_launch.hpp", "../../include/qc.h"]
 OP_SOURCE = {
-    **{o: "k_encode.hip" for o in ("uniform_enc", "qsgd_enc", "sign_enc", "int2_enc", "stoch4_enc", "tern_enc",
+    **{o: "k_encode.hpp" for o in ("uniform_enc", "qsgd_enc", "sign_enc", "int2_enc", "stoch4_enc", "tern_enc",
                                    "shared_absmax", "shared_enc", "list_enc", "list_enc_per_tensor")},
     "fp8_enc": "k_fp8.hip",
     **{o: "k_decode.hip" for o in ("uniform_dec", "fp8_dec", "qsgd_dec", "sign_dec", "int2_dec", "tern_dec",

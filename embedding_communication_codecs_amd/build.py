@@ -33,7 +33,7 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
 ]
-SOURCES = ["k_encode.hip", "k_fp8.hip", "k_decode.hip", "k_accumulate.hip", "k_vote.hip", "k_shared_sum.hip",
+SOURCES = ["k_encode.hip", "k_encode_codecs.hip", "k_encode_list.hip", "k_encode_list_codecs.hip", "k_fp8.hip", "k_decode.hip", "k_accumulate.hip", "k_vote.hip", "k_shared_sum.hip",
            "k_topk.hip", "qc_api.cpp"]
 
 
