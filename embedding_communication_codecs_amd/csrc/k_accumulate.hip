@@ -174,6 +174,45 @@ __device__ __forceinline__ void add_chunk_exact(float (&a)[16], const ChunkBits<
     }
 }
 
+// 2-bit uniform codes through a per-wave table in LDS.  A 2-bit code has
+// four decoded values per (worker, bucket); lanes 0-3 write them (computed
+// exactly as the decoder computes them) to the wave's 256-byte-aligned
+// table, and a term becomes one v_perm (the code, times 4, as the low
+// address byte over the table's base), one ds_read_b32 and one add, where
+// the arithmetic path takes a conversion, a multiply and two adds.  The LDS
+// pipe works beside the VALU, which bounds 2-bit sums, so the codes of
+// residue r < TAB_NV (elements 4q + r of a chunk) keep the arithmetic path
+// and the rest go through the table.  Measured on the 64-worker sum of
+// 2^26 elements in buckets of 2,048: 417 us all-arithmetic (statistics in
+// scalar registers), 383 us with them in vector registers, 355 us with a
+// quarter of the terms on the VALU (TAB_NV = 1); 397 us with every term
+// through the table, 376 us with three quarters on the VALU.
+constexpr int TAB_NV = 1;
+typedef __attribute__((address_space(3))) float lds_f32;
+__device__ __forceinline__ uint32_t lds_addr(float* p) { return (uint32_t)(uintptr_t)(lds_f32*)p; }
+__device__ __forceinline__ float lds_load(uint32_t a) { return *(const lds_f32*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_store(uint32_t a, float v) { *(lds_f32*)(uintptr_t)a = v; }
+
+__device__ __forceinline__ void add_chunk_u2_tab(float (&a)[16], uint32_t w, float s, float z, uint32_t tbase) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r < TAB_NV) {
+            const uint32_t sp = and_mask(w >> (2 * r), 0x03030303u);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float p = byte_f(sp, q) * s;
+                a[4 * q + r] = a[4 * q + r] + (p + z);
+            }
+        } else {
+            // byte q = 4 * code(4q + r)
+            const uint32_t sp4 = and_mask(r == 0 ? w << 2 : w >> (2 * r - 2), 0x0C0C0C0Cu);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                a[4 * q + r] = a[4 * q + r] + lds_load(__builtin_amdgcn_perm(tbase, sp4, 0x07060500u | (uint32_t)q));
+        }
+    }
+}
+
 constexpr bool has_zero(int F) { return F == A_U8 || F == A_U4 || F == A_U2; }
 
 // Per-(worker, bucket) statistics.  When a bucket spans whole waves they are
@@ -237,8 +276,9 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                                            int64_t pbytes, float* __restrict__ acc, int32_t accumulate,
                                            uint8_t* __restrict__ rq_codes, int64_t rq_pbytes,
                                            float* __restrict__ rq_scale, float* __restrict__ rq_zero,
-                                           int64_t bk, int64_t gb, float* lds) {
+                                           int64_t bk, int64_t gb, float* lds, uint32_t tbase) {
     constexpr int K = G::K, LPB = G::LPB, UW = 2;
+    constexpr bool TAB = F == A_U2 && Stats<G, F>::WAVE_UNIFORM;
     const int64_t base = bk * (int64_t)G::B + lane_offset<G>();
 
     float a[K][16];
@@ -283,11 +323,27 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
         float s, z;
         st.get(scale, zero, ng, gb, w, s, z);
         if constexpr (F == A_QSGD) z = s / 7.0f;
-        if (needs_exact_path<F>(s, z)) {
+        const bool exact = needs_exact_path<F>(s, z);
+        // Wave-uniform statistics arrive in scalar registers (v_readlane).
+        // On gfx950 a VALU op that reads a scalar register issues at about
+        // half the rate of one whose operands are all vector registers
+        // (measured: v_add_f32 38 vs 67 T lane-ops/s), and the term loop is
+        // VALU-bound for sub-byte codes, so s and z are copied to vector
+        // registers once per worker.
+        if constexpr (Stats<G, F>::WAVE_UNIFORM) asm volatile("" : "+v"(s), "+v"(z));
+        if (exact) {
             if constexpr (F == A_QSGD || F == A_TER) {
 #pragma unroll
                 for (int k = 0; k < K; ++k) add_chunk_exact<F>(a[k], c[k], s, z);
             }
+        } else if constexpr (TAB) {
+            if (lane_id() < 4) {
+                // the decoded value of code l, rounded as the decoder rounds it
+                const float p = (float)lane_id() * s;
+                lds_store(tbase + 4u * (uint32_t)lane_id(), p + z);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) add_chunk_u2_tab(a[k], c[k].v.x, s, z, tbase);
         } else {
 #pragma unroll
             for (int k = 0; k < K; ++k) add_chunk<F>(a[k], c[k], s, z);
@@ -411,6 +467,10 @@ k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale
               int64_t pbytes, float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,
               int64_t rq_pbytes, float* __restrict__ rq_scale, float* __restrict__ rq_zero) {
     __shared__ float lds[G::W];
+    // one 256-byte-aligned decode table per wave (2-bit uniform codes; the
+    // array is dropped from kernels that do not read it)
+    __shared__ __align__(256) float tab[G::THREADS / WAVE][64];
+    const uint32_t tbase = lds_addr(&tab[wave_id()][0]);
 
     // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs,
     // so block b runs on XCD b%8; give each XCD a contiguous bucket range.
@@ -429,10 +489,10 @@ k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale
         const int64_t gb = bks >> tshift;
         if ((bks + 1) * (int64_t)G::B <= n)
             acc_bucket<G, F, RQBITS, RQ, true>(codes, scale, zero, m, n, ng, pbytes, acc, accumulate,
-                                               rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds);
+                                               rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds, tbase);
         else
             acc_bucket<G, F, RQBITS, RQ, false>(codes, scale, zero, m, n, ng, pbytes, acc, accumulate,
-                                                rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds);
+                                                rq_codes, rq_pbytes, rq_scale, rq_zero, bks, gb, lds, tbase);
     }
 }
 
