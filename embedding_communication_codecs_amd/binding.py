@@ -23,7 +23,7 @@ QC_F32, QC_BF16 = 0, 1
 QC_MIN_BUCKET, QC_MAX_BUCKET, QC_MAX_WORKERS = 64, 65536, 65535
 QC_INDEX_SHIFT = 12
 QC_MAX_LIST_BUCKET = 32768
-QC_MAX_TOPK_BUCKET = 8192
+QC_MAX_TOPK_BUCKET = 65536
 
 EXPORTS = (
     "qc_encode_uniform", "qc_encode_uniform_stochastic", "qc_encode_uniform_multi", "qc_encode_fp8_rowwise",
@@ -31,7 +31,7 @@ EXPORTS = (
     "qc_encode_ternary", "qc_encode_sign", "qc_bucket_absmax", "qc_absmax_combine", "qc_encode_int8_shared",
     "qc_sum_int8_shared", "qc_tensor_index", "qc_encode_topk", "qc_decode_topk", "qc_topk_accumulate",
     "qc_encode_uniform_stochastic_multi", "qc_encode_qsgd_multi", "qc_encode_ternary_multi", "qc_encode_sign_multi",
-    "qc_bucket_absmax_multi", "qc_encode_int8_shared_multi",
+    "qc_bucket_absmax_multi", "qc_encode_int8_shared_multi", "qc_encode_topk_multi",
     "qc_decode", "qc_decode_multi", "qc_dequant_accumulate", "qc_majority_vote", "qc_payload_bytes", "qc_status_str",
 )
 
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "qc_encode_sign_multi": [P, I32, P, P, I32, I64, P, I32, P, P, P],
             "qc_bucket_absmax_multi": [P, P, P, I32, I64, P, I32, P, P],
             "qc_encode_int8_shared_multi": [P, P, P, I32, I64, P, I32, P, P, P, P],
+            "qc_encode_topk_multi": [P, P, P, I32, I64, P, I32, I32, P, P, P],
             "qc_decode_multi": [I32, P, P, P, I64, I32, I32, P, P, P, I32, P],
             "qc_encode_fp8_rowwise": [P, I64, I32, P, P, P],
             "qc_encode_qsgd": [P, P, I64, I32, I32, U64, U64, P, P, P],
@@ -377,6 +378,13 @@ def qc_encode_topk(x, ef, n, bucket, k, values, indices, stream=None):
     _check(lib().qc_encode_topk(_ptr(x, 4 * n, "x"), _ptr(ef, 4 * n, "ef"), n, bucket, k,
                                 _ptr(values, 4 * slots, "values"), _ptr(indices, 4 * slots, "indices"),
                                 _stream(stream)))
+
+
+def qc_encode_topk_multi(xs, offsets, seg_first, ntensors, n, ef, bucket, k, values, indices, stream=None):
+    slots = nbuckets(n, bucket) * k if n > 0 and bucket > 0 and k > 0 else 0
+    _check(lib().qc_encode_topk_multi(
+        *_list_args(xs, offsets, seg_first, ntensors, n), _ptr(ef, 4 * n, "ef"), bucket, k,
+        _ptr(values, 4 * slots, "values"), _ptr(indices, 4 * slots, "indices"), _stream(stream)))
 
 
 def qc_decode_topk(values, indices, n, bucket, k, out, stream=None):

@@ -132,9 +132,9 @@ namespace {
 // the host can: pointers present and aligned), the bucket, and n.  Returns
 // QC_OK with `l` filled, or the error status.
 int check_list(const void* const* xs, const int64_t* offsets, const int32_t* seg_first, int32_t ntensors,
-               int64_t n, int32_t bucket, qc::ListSrc& l) {
+               int64_t n, int32_t bucket, qc::ListSrc& l, int32_t max_bucket = QC_MAX_LIST_BUCKET) {
     if (n < 0 || ntensors < 1 || bad_bucket(bucket)) return QC_ERR_ARG;
-    if (bucket > QC_MAX_LIST_BUCKET) return QC_ERR_UNSUPPORTED;
+    if (bucket > max_bucket) return QC_ERR_UNSUPPORTED;
     if (n == 0) return QC_OK;  // an empty call: the caller returns before using l
     if (!xs || !offsets || !seg_first) return QC_ERR_ARG;
     if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
@@ -444,6 +444,20 @@ int qc_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t
     if (ceil_div(n, bucket) > kMaxBuckets) return QC_ERR_ARG;
     if (misaligned(x) || misaligned(ef) || misaligned4(values) || misaligned4(indices)) return QC_ERR_ALIGN;
     return launched(qc::launch_encode_topk(x, ef, n, bucket, k, values, indices, hs(stream)));
+}
+
+int qc_encode_topk_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t k, float* values,
+                         uint32_t* indices, qc_stream_t stream) {
+    qc::ListSrc l;
+    int st = check_topk(n, bucket, k);
+    if (st == QC_OK)
+        st = check_list(reinterpret_cast<const void* const*>(xs), offsets, seg_first, ntensors, n, bucket, l,
+                        QC_MAX_TOPK_BUCKET);
+    if (st != QC_OK || n == 0) return st;
+    if (!values || !indices) return QC_ERR_ARG;
+    if (misaligned(ef) || misaligned4(values) || misaligned4(indices)) return QC_ERR_ALIGN;
+    return launched(qc::launch_encode_topk_list(l, ef, bucket, k, values, indices, hs(stream)));
 }
 
 int qc_decode_topk(const float* values, const uint32_t* indices, int64_t n, int32_t bucket, int32_t k,

@@ -193,6 +193,10 @@ int qc_encode_uniform_multi(const float* const* xs, const int64_t* offsets, cons
  *                                        alignment
  *   qc_bucket_absmax_multi               qc_bucket_absmax
  *   qc_encode_int8_shared_multi          qc_encode_int8_shared
+ *   qc_encode_topk_multi                 qc_encode_topk: buckets up to
+ *                                        QC_MAX_TOPK_BUCKET (65,536; its
+ *                                        kernels hold no bucket in
+ *                                        registers)
  */
 int qc_encode_uniform_stochastic_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
                                        int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t bits,
@@ -213,6 +217,9 @@ int qc_bucket_absmax_multi(const float* const* xs, const int64_t* offsets, const
 int qc_encode_int8_shared_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
                                 int32_t ntensors, int64_t n, float* ef, int32_t bucket, const float* amax,
                                 uint8_t* codes, float* scale, qc_stream_t stream);
+int qc_encode_topk_multi(const float* const* xs, const int64_t* offsets, const int32_t* seg_first,
+                         int32_t ntensors, int64_t n, float* ef, int32_t bucket, int32_t k, float* values,
+                         uint32_t* indices, qc_stream_t stream);
 
 /*
  * Rowwise FP8 (OCP E4M3FN) for embedding-lookup payloads: one byte per
@@ -451,7 +458,7 @@ int qc_sum_int8_shared(const uint8_t* codes, int32_t m, int64_t n, int32_t bucke
  * Errors: ARG (NULL x/values/indices, n < 0, bad bucket, k outside
  *         [1, bucket]), UNSUPPORTED (bucket > QC_MAX_TOPK_BUCKET), ALIGN.
  */
-#define QC_MAX_TOPK_BUCKET 8192
+#define QC_MAX_TOPK_BUCKET 65536
 int qc_encode_topk(const float* x, float* ef, int64_t n, int32_t bucket, int32_t k, float* values,
                    uint32_t* indices, qc_stream_t stream);
 

@@ -370,7 +370,7 @@ def test_topk_errors(qc):
     for k in (0, -1, 513):
         assert call(qc, f, A, A, 1000, 512, k, A, A, None) == qc.QC_ERR_ARG, k
     assert call(qc, f, A, A, 1000, 500, 8, A, A, None) == qc.QC_ERR_ARG
-    assert call(qc, f, A, A, 100000, 16384, 8, A, A, None) == qc.QC_ERR_UNSUPPORTED
+    assert call(qc, f, A, A, 100000, 131072, 8, A, A, None) == qc.QC_ERR_ARG
     for pos in (0, 5, 6):
         args = list(ok)
         args[pos] = NULL
@@ -380,6 +380,25 @@ def test_topk_errors(qc):
         args[pos] = bad
         assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
     assert call(qc, f, NULL, NULL, 0, 512, 8, NULL, NULL, None) == qc.QC_OK
+    f = "qc_encode_topk_multi"
+    ok = (A, A, A, 5, 1000, A, 512, 8, A, A, None)
+    for pos in (0, 1, 2, 8, 9):
+        args = list(ok)
+        args[pos] = NULL
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, pos
+    for k in (0, 513):
+        args = list(ok)
+        args[7] = k
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, k
+    for bucket in (100, 32, 131072):
+        args = list(ok)
+        args[6] = bucket
+        assert call(qc, f, *args) == qc.QC_ERR_ARG, bucket
+    for pos, bad in ((0, A + 4), (1, A + 4), (2, A + 2), (5, MIS), (8, A + 2), (9, A + 1)):
+        args = list(ok)
+        args[pos] = bad
+        assert call(qc, f, *args) == qc.QC_ERR_ALIGN, pos
+    assert call(qc, f, A, A, A, 5, 0, NULL, 512, 8, NULL, NULL, None) == qc.QC_OK
     f = "qc_decode_topk"
     assert call(qc, f, A, A, 1000, 512, 600, A, None) == qc.QC_ERR_ARG
     assert call(qc, f, A, A, 1000, 512, 8, NULL, None) == qc.QC_ERR_ARG

@@ -1,6 +1,6 @@
 """GPU parity for every encoder's tensor-list form: stochastic uniform,
-QSGD, TernGrad, sign (fp32 and bf16 tensors), and the shared-scale
-statistic and encoder each encode a list of tensors, read in place,
+QSGD, TernGrad, sign (fp32 and bf16 tensors), the shared-scale statistic
+and encoder, and top-k each encode a list of tensors, read in place,
 exactly as the oracle encodes their concatenation (codes, statistics and
 the residual, bit for bit).  Tensor sizes include 0, 1 and sizes that are
 not multiples of 4; tensors start at addresses that are not 16-byte
@@ -120,6 +120,26 @@ def test_qsgd_and_ternary_multi(qc, ora, bucket, count):
     p, s = ora.encode_ternary(flat, ef_h, bucket, 0x5445524E, 0)
     assert bits_equal(words.host(), p) and bits_equal(scale.f32(), s), first_diff(words.host(), p)
     assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
+
+
+@pytest.mark.parametrize("bucket,count", CASES + [(65536, 5), (16384, 40)])
+def test_topk_multi(qc, ora, bucket, count):
+    host = inputs(count, bucket, 700 + count)
+    flat = ora.concat(host)
+    n = flat.size
+    nb = qc.nbuckets(n, bucket)
+    _, views = carve(host)
+    t = qc.TensorTable(views)
+    for k in sorted({1, 5, max(1, bucket // 100), bucket}):
+        ef_h = synth.host_normal(n, 1e-4, seed=count + k)
+        ef_d = dev_ef(ef_h)
+        vals, idx = out_f32(nb * k), Out(4 * nb * k)
+        qc.qc_encode_topk_multi(t.xs, t.offsets, t.seg_first, t.ntensors, n, ef_d.t, bucket, k, vals.t, idx.t)
+        sync()
+        pv, pi = ora.encode_topk(flat, ef_h, bucket, k)
+        assert bits_equal(idx.host().view(np.uint32), pi), (k, first_diff(idx.host().view(np.uint32), pi))
+        assert bits_equal(vals.f32(), pv), (k, first_diff(vals.f32(), pv))
+        assert bits_equal(ef_d.f32(), ef_h), (k, first_diff(ef_d.f32(), ef_h))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

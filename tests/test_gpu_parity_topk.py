@@ -3,8 +3,9 @@ the candidate path for small k and the radix select; pairs in index order,
 error feedback), the decoder (scatter into a dense vector)
 and the sum of several workers' sparse payloads, each called through the C
 ABI and compared bit for bit with the CPU oracle on the same seeded inputs:
-every bucket size, k from 1 to the whole bucket, short last buckets, many
-equal magnitudes (ties go to the smaller index), signed zeros."""
+every bucket size (16,384 to 65,536 through the streaming encoder and the
+tiled decoder and sums), k from 1 to the whole bucket, short last buckets,
+many equal magnitudes (ties go to the smaller index), signed zeros."""
 import numpy as np
 import pytest
 
@@ -13,7 +14,7 @@ from gpu_util import Out, bits_equal, dev, dev_ef, first_diff, need_gpu, out_f32
 
 pytestmark = pytest.mark.gpu
 
-BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192]
+BUCKETS = [64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
 
 
 @pytest.fixture(scope="module")
@@ -116,7 +117,8 @@ def test_topk_many_candidates_fall_back(qc, ora, k):
     assert bits_equal(ef_d.f32(), ef_h)
 
 
-@pytest.mark.parametrize("bucket,k", [(64, 1), (64, 64), (1024, 10), (8192, 8), (8192, 5000)])
+@pytest.mark.parametrize("bucket,k", [(64, 1), (64, 64), (1024, 10), (8192, 8), (8192, 5000), (16384, 100),
+                                      (32768, 32768), (65536, 3000)])
 def test_topk_decode(qc, ora, bucket, k):
     n = 2 * bucket + 13
     x = gradient_like(n, seed=k, ties=True)
@@ -128,7 +130,7 @@ def test_topk_decode(qc, ora, bucket, k):
     assert bits_equal(out.f32(), want), first_diff(out.f32(), want)
 
 
-@pytest.mark.parametrize("bucket,k", [(64, 3), (1024, 10), (8192, 8), (4096, 2048)])
+@pytest.mark.parametrize("bucket,k", [(64, 3), (1024, 10), (8192, 8), (4096, 2048), (32768, 8), (65536, 300)])
 @pytest.mark.parametrize("m", [1, 3, 64])
 def test_topk_accumulate(qc, ora, bucket, k, m):
     n = 2 * bucket + 13
@@ -155,7 +157,7 @@ def test_topk_accumulate(qc, ora, bucket, k, m):
 def test_topk_random_shapes(qc, ora):
     rng = np.random.default_rng(404)
     for trial in range(40):
-        bucket = int(2 ** rng.integers(6, 14))
+        bucket = int(2 ** rng.integers(6, 17))
         n = int(rng.integers(1, 4 * bucket))
         k = int(rng.integers(1, bucket + 1)) if trial % 3 else int(rng.integers(1, 8))
         x = gradient_like(n, seed=trial, ties=bool(trial % 2))
@@ -201,7 +203,8 @@ def sparse_workers(m, n, bucket, k, rng, mode):
 
 @pytest.mark.parametrize("mode", ["random", "same", "alias", "mixed"])
 @pytest.mark.parametrize("bucket,k,m,nbk", [(64, 1, 600, 3), (256, 63, 9, 9), (1024, 10, 100, 17),
-                                            (4096, 4, 64, 5), (8192, 33, 20, 2), (2048, 1, 3, 1)])
+                                            (4096, 4, 64, 5), (8192, 33, 20, 2), (2048, 1, 3, 1),
+                                            (32768, 5, 40, 2)])
 def test_topk_sum_conflicts(qc, ora, mode, bucket, k, m, nbk):
     """The one-wave sum for k < 64: several chunks of 256 pairs per bucket,
     one worker per pair (k = 1, 600 workers), every worker on the same
