@@ -70,14 +70,33 @@ __device__ __forceinline__ uint32_t fp8_pack4_fast(f32x4 v, float sc, bool& fix)
     const uint32_t nmin = min(min(near[0], near[1]), min(near[2], near[3]));
     const float ymin = fminf(fminf(fabsf(y[0]), fabsf(y[1])), fminf(fabsf(y[2]), fabsf(y[3])));
     fix |= sc != 0.0f && (nmin <= 16u || ymin < 0x1p-6f || !(sc >= 0x1p-126f));
+    // where the word is kept (no fix-up), every |y| >= 2^-6: normal codes only
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) word |= e4m3_encode(fminf(fmaxf(y[j], -448.0f), 448.0f)) << (8 * j);
+    for (int j = 0; j < 4; ++j) word |= e4m3_encode_normal(fminf(fmaxf(y[j], -448.0f), 448.0f)) << (8 * j);
     return sc == 0.0f ? 0u : word;
 }
 
 __device__ __forceinline__ float amax4(f32x4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// The row maximum of |x| as the reference loop takes it (a running maximum
+// from +0 that a NaN never replaces, so an all-NaN row gives +0), in
+// unsigned integer form: key(x) = (bits(x) << 1) + 0x00FFFFFE drops the
+// sign and maps |x| from +0 to +inf, in order, onto [0x00FFFFFE,
+// 0xFFFFFFFE], while every NaN wraps below 0x00FFFFFE.  Integer maxima
+// take one instruction per cross-lane step (the DPP move folds into
+// v_max_u32); float maxima took four (each operand is quieted first).
+constexpr uint32_t kKeyZero = 0x00FFFFFEu;
+__device__ __forceinline__ uint32_t amax_key(float x) { return (__float_as_uint(x) << 1) + kKeyZero; }
+__device__ __forceinline__ uint32_t amax4_key(f32x4 v) {
+    const uint32_t a = amax_key(v.x), b = amax_key(v.y), c = amax_key(v.z), d = amax_key(v.w);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+__device__ __forceinline__ float amax_of_key(uint32_t k) {
+    return k < kKeyZero ? 0.0f : __uint_as_float((k - kKeyZero) >> 1);
 }
 
 // The payload is rows*dim bytes rounded up to 16; whoever owns the last row
@@ -110,7 +129,7 @@ __device__ __forceinline__ void fp8_rows(const float* __restrict__ x, int64_t ro
     bool fix = false;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-        amax[g] = group_max<LPR>(amax4(v[g]));
+        amax[g] = amax_of_key(group_max_u32<LPR>(amax4_key(v[g])));
         sc[g] = fp8_row_scale_fast(amax[g], fix);
         word[g] = fp8_pack4_fast(v[g], sc[g], fix);
     }

@@ -83,7 +83,7 @@ template <int OFF>
 __device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
     static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8, "row step");
     constexpr int ctrl = OFF == 1 ? 0xB1 : (OFF == 2 ? 0x4E : (OFF == 4 ? 0x141 : 0x140));
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, true);
 }
 
 template <int G, class T, class Op>
@@ -119,6 +119,12 @@ __device__ __forceinline__ float group_min(float v) {
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
     return group_reduce<G>(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+// Unsigned maximum over a group (a DPP move folds into v_max_u32).
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+    return group_reduce<G>(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 template <int G>
@@ -183,6 +189,16 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     const uint32_t normal = (rounded >> 20) - (120u << 3);
     const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
     return sign | (a >= 0x3C800000u ? normal : sub);
+}
+
+// e4m3_encode for |y| >= 2^-6 (the normal codes), where the subnormal
+// branch above is never taken.
+__device__ __forceinline__ uint32_t e4m3_encode_normal(float y) {
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((rounded >> 20) - (120u << 3));
 }
 
 // Exact E4M3 -> fp32: normal codes rebias the exponent by +120 and place

@@ -146,6 +146,27 @@ def test_fp8_rounding_edges(qc, ora):
     assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
 
 
+@pytest.mark.parametrize("dim", [128, 96])
+def test_fp8_row_maximum_ignores_nan(qc, ora, dim):
+    """The row maximum is a running maximum of |x| from +0 that a NaN never
+    replaces: an all-NaN row has amax 0, scale 0 and all codes 0; rows of
+    -0 and of the largest finite values, and a row whose maximum sits in the
+    last lane, sit beside it."""
+    rows = 64
+    x = synth.host_embedding_rows(rows, dim, 0.05, 0.01, 50.0, seed=dim)
+    xr = x.reshape(rows, dim)
+    xr[3] = np.float32(np.nan)
+    xr[4] = -np.float32(np.nan)
+    xr[5] = -0.0
+    xr[6] = np.float32(3.4028235e38) * np.where(np.arange(dim) % 2, -1, 1)
+    xr[7, -1] = 9.0
+    codes, scale = run_fp8(qc, x, rows, dim)
+    p, s = ora.encode_fp8_rowwise(x, rows, dim)
+    assert s[3] == 0.0 and s[4] == 0.0 and not p[3 * dim: 5 * dim].any()
+    assert bits_equal(scale.f32(), s), first_diff(scale.f32(), s)
+    assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_fp8_conversion_sweep(qc, ora, seed):
     """4M random fp32 bit patterns in [-448, 448] through rows with scale 1."""
