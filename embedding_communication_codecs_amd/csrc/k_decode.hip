@@ -113,11 +113,29 @@ struct TensorOuts {
     const int32_t* __restrict__ seg;
     int32_t T;
     int32_t lo = 0, hi = 0;
+    // A tile inside one tensor (the common case: tensors are usually much
+    // larger than a tile) stores through that tensor's pointer without
+    // looking anything up per store; the search below costs a few dependent
+    // loads of the tables per store.
+    float* one = nullptr;  // element g of the tile's only tensor is one[g]
+    int64_t one_end = 0;
 
-    __device__ __forceinline__ void prepare(int64_t g0, int64_t g1) { tensor_range(off, seg, T, g0, g1, lo, hi); }
+    __device__ __forceinline__ void prepare(int64_t g0, int64_t g1) {
+        tensor_range(off, seg, T, g0, g1, lo, hi);
+        one = nullptr;
+        if (lo == hi) {
+            one_end = off[lo + 1];
+            one = outs[lo] - off[lo];
+        }
+    }
 
     template <bool FULL>
     __device__ __forceinline__ void store(int64_t i, int64_t n, const float (&o)[4]) const {
+        if (one != nullptr && (FULL || i + 4 <= n) && i + 4 <= one_end &&
+            (reinterpret_cast<uintptr_t>(one + i) & 15u) == 0) {
+            st_f4(one + i, f32x4{o[0], o[1], o[2], o[3]});
+            return;
+        }
         int32_t t = tensor_of(off, lo, hi, i);
         float* p = outs[t] + (i - off[t]);
         if ((FULL || i + 4 <= n) && i + 4 <= off[t + 1] && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
