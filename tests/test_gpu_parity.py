@@ -146,7 +146,7 @@ def test_fp8_rounding_edges(qc, ora):
     assert bits_equal(codes.host(), p), first_diff(codes.host(), p)
 
 
-@pytest.mark.parametrize("dim", [128, 96])
+@pytest.mark.parametrize("dim", [4, 16, 128, 256, 96])
 def test_fp8_row_maximum_ignores_nan(qc, ora, dim):
     """The row maximum is a running maximum of |x| from +0 that a NaN never
     replaces: an all-NaN row has amax 0, scale 0 and all codes 0; rows of
