@@ -3,7 +3,7 @@
 // in the same pass.
 //
 // Each lane owns 16 consecutive elements per chunk (one 16-byte load of
-// INT8/FP8 codes per worker, 8 bytes for 4-bit, 2 bytes for sign) and keeps
+// INT8/FP8 codes per worker, 8 bytes for 4-bit, 4 for 2-bit, 2 for sign) and keeps
 // their fp32 sums in registers while it walks the workers in order, so the
 // result is bit-identical to adding the decoded terms one worker at a time.
 // Two workers' loads are kept in flight while terms are added.  A bucket
@@ -13,7 +13,9 @@
 //
 // The per-(worker, bucket) scale and zero are uniform across a wave when a
 // bucket spans whole waves; one vector load brings 64 workers' values into
-// a register across the wave (see Stats).  Blocks are mapped to buckets XCD
+// a register across the wave (see Stats); each worker's pair is then
+// copied to vector registers, and 2-bit uniform terms read most of their
+// decoded values from a per-wave table in LDS.  Blocks are mapped to buckets XCD
 // by XCD (consecutive buckets on one XCD), so neighbouring buckets'
 // statistics share that XCD's L2 lines.
 //
