@@ -606,8 +606,11 @@ def time_alone(torch, ops, names, sizes, per_op, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 200 steps keep the GPU busy for several seconds (about 1 s of the step,
+    # 4 s of the extensions and 5 s of the ops timed alone), long enough for
+    # an outside utilization sampler to see it
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default=",".join(ORDER + EXT_ORDER), help="comma-separated subset of ops to run")
     ap.add_argument("--no-extensions", action="store_true", help="skip the low-bit extension ops")
