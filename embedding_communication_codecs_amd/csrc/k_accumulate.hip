@@ -215,14 +215,6 @@ __device__ __forceinline__ void add_chunk_u2_tab(float (&a)[16], uint32_t w, flo
     }
 }
 
-// Orders a wave's LDS accesses before and after it (lanes exchange data
-// through LDS within one wave; a wave's LDS instructions run in order).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 constexpr bool has_zero(int F) { return F == A_U8 || F == A_U4 || F == A_U2; }
 
 // Per-(worker, bucket) statistics.  When a bucket spans whole waves they are
@@ -382,31 +374,16 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
             if (w0 + u < cend) add_worker(w0 + u, slot[u]);
     }
 
-    // A lane's 16 sums are 64 contiguous bytes, so a store instruction
-    // straight from registers covers every fourth 16-byte piece of a 4 KiB
-    // span and touches 32 lines.  Full tiles of whole-wave buckets pass
-    // the sums through a 4 KiB LDS buffer per wave instead, so each store
-    // instruction writes 1 KiB contiguously (8 lines), with streaming
-    // stores; the LDS round trip is one write and one read per chunk.
-    // (Not for the 2-bit sum with requantization: the buffer's addresses
-    // took it from 127 to 131 registers and 4 to 3 waves per SIMD, 11%
-    // slower; the others gained 4-6%.)
+    // A lane's 16 sums are 64 contiguous bytes: full tiles of whole-wave
+    // buckets store each chunk's 4 KiB span through the wave's LDS buffer
+    // (store_wave_span16: 1 KiB-contiguous streaming stores).  Not for the
+    // 2-bit sum with requantization: the buffer's addresses took it from
+    // 127 to 131 registers and 4 to 3 waves per SIMD, 11% slower; the
+    // others gained 4-6%.
     if constexpr (FULL && LPB == WAVE && !(F == A_U2 && RQ)) {
-        const int l = lane_id();
         const int64_t c0 = bk * (int64_t)G::B + (G::W > 1 ? (int64_t)wave_id() * G::SUB : 0);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4*>(xw + 16 * l + 4 * q) =
-                    f32x4{a[k][4 * q], a[k][4 * q + 1], a[k][4 * q + 2], a[k][4 * q + 3]};
-            wave_lds_sync();
-            const int64_t ck = c0 + (int64_t)k * LPB * 16;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                st_f4(acc + ck + 256 * q + 4 * l, *reinterpret_cast<const f32x4*>(xw + 256 * q + 4 * l));
-            wave_lds_sync();  // the buffer is rewritten for the next chunk
-        }
+        for (int k = 0; k < K; ++k) store_wave_span16(acc + c0 + (int64_t)k * LPB * 16, a[k], xw);
     } else {
     // Otherwise acc is written with plain stores, which L2 merges into whole
     // lines (streaming stores would not be merged).

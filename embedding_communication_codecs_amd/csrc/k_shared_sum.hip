@@ -39,7 +39,7 @@ template <bool FULL, bool ISUM, bool OUT>
 __device__ __forceinline__ void sum_tile(const uint8_t* __restrict__ codes, int32_t m, int64_t n,
                                          int64_t nchunks, int64_t pbytes, int gshift,
                                          const float* __restrict__ scale, int32_t* __restrict__ isum,
-                                         int32_t accumulate, float* __restrict__ out, int64_t t0) {
+                                         int32_t accumulate, float* __restrict__ out, int64_t t0, float* xw) {
     int32_t a[U][16];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -109,7 +109,10 @@ __device__ __forceinline__ void sum_tile(const uint8_t* __restrict__ codes, int3
             float o[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) o[j] = (float)a[u][j] * sc;
-            if (whole) {
+            if constexpr (FULL) {
+                // the wave's 64 chunks are one 1,024-element span
+                store_wave_span16(out + (t0 + u * TPB + wave_id() * WAVE) * 16, o, xw);
+            } else if (whole) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     *reinterpret_cast<f32x4*>(out + i + 4 * q) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
@@ -130,11 +133,14 @@ k_sum_int8_shared(const uint8_t* __restrict__ codes, int32_t m, int64_t n, int64
                   float* __restrict__ out) {
     const int64_t nchunks = (n + 15) >> 4;
     constexpr int64_t TILE = (int64_t)TPB * U;
+    // one 4 KiB buffer per wave for the output's contiguous stores
+    __shared__ __align__(16) float xbuf[TPB / WAVE][1024];
+    float* xw = &xbuf[wave_id()][0];
     for (int64_t t0 = (int64_t)blockIdx.x * TILE; t0 < nchunks; t0 += (int64_t)gridDim.x * TILE) {
         if ((t0 + TILE) * 16 <= n)
-            sum_tile<true, ISUM, OUT>(codes, m, n, nchunks, pbytes, gshift, scale, isum, accumulate, out, t0);
+            sum_tile<true, ISUM, OUT>(codes, m, n, nchunks, pbytes, gshift, scale, isum, accumulate, out, t0, xw);
         else
-            sum_tile<false, ISUM, OUT>(codes, m, n, nchunks, pbytes, gshift, scale, isum, accumulate, out, t0);
+            sum_tile<false, ISUM, OUT>(codes, m, n, nchunks, pbytes, gshift, scale, isum, accumulate, out, t0, xw);
     }
 }
 

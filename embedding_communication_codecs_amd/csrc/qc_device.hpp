@@ -211,6 +211,41 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
+// ------------------------------------------------- wave-span stores
+// Orders a wave's LDS accesses before and after it (lanes exchange data
+// through LDS within one wave; a wave's LDS instructions run in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Lane l holds elements [16l, 16l + 16) of a 1,024-element span at dst.
+// Stored from registers, each instruction would cover every fourth
+// 16-byte piece of the 4 KiB span and touch 32 cache lines (the compute
+// units' limit on outstanding requests is what the streaming kernels run
+// into); passed through the wave's 4 KiB LDS buffer xw, each of the four
+// store instructions writes 1 KiB contiguously (8 lines), with streaming
+// stores.  All 64 lanes must be active and the whole span inside dst.
+// Piece q (elements 4q..4q+3) of this lane's 16 into the wave's buffer.
+__device__ __forceinline__ void span16_put(float* xw, int q, f32x4 v) {
+    *reinterpret_cast<f32x4*>(xw + 16 * lane_id() + 4 * q) = v;
+}
+// Every lane's 16 elements are in xw: store the span from it.
+__device__ __forceinline__ void span16_store(float* __restrict__ dst, float* xw) {
+    const int l = lane_id();
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        st_f4(dst + 256 * q + 4 * l, *reinterpret_cast<const f32x4*>(xw + 256 * q + 4 * l));
+    wave_lds_sync();  // xw may be rewritten right after
+}
+__device__ __forceinline__ void store_wave_span16(float* __restrict__ dst, const float (&v)[16], float* xw) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) span16_put(xw, q, f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]});
+    span16_store(dst, xw);
+}
+
 // --------------------------------------------------------------- misc
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
