@@ -75,7 +75,7 @@ __device__ __forceinline__ float neg_if_bit(float m, uint32_t w, int b) {
 // rounded once in fp32 exactly as decode-then-add would round it.  Sub-byte
 // codes are first spread one per byte (a few shifts and masks per word), so
 // each code converts with a byte conversion instead of a bitfield extract.
-// For QSGD `z` is d = norm/7.
+// For QSGD `z` is d = norm/7, for TernGrad s/2.
 template <int F>
 __device__ __forceinline__ void add_chunk(float (&a)[16], const ChunkBits<F>& c, float s, float z) {
     const uint32_t words[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
@@ -109,16 +109,23 @@ __device__ __forceinline__ void add_chunk(float (&a)[16], const ChunkBits<F>& c,
             a[j] = a[j] + (p + z);
         }
     } else if constexpr (F == A_TER) {
-        // The term is 0 or +-s, so fma(f, s, a) with f in {0, 1, -1} is the
-        // exact sum rounded once, as a + DQ is.  f is the 2-bit code read as
-        // a signed field, after clearing bit 1 where bit 0 is clear (the
-        // value of the never-emitted code 2, like code 0, is +0).
+        // The term is 0 or +-s, so fma(f, s/2, a) with f in {0, 2, -2} is
+        // the exact sum rounded once, as a + DQ is (z = s/2, exact for the
+        // scales this path takes).  A code whose bit 1 is cleared where its
+        // bit 0 is clear (the never-emitted code 2, like code 0, is +0) is
+        // the top two bits of an fp16 number with nothing below them:
+        // 0x0000 = +0, 0x4000 = 2, 0xC000 = -2.  One shift and one mask put
+        // codes j and j + 8 at the top of the two halves of a word, and each
+        // half feeds v_fma_mix_f32 (fp16 operand, fp32 arithmetic) directly:
+        // an fma per term and one shift or mask per two terms, against a
+        // bitfield extract, a conversion and an fma.
         const uint32_t w = words[0];
         const uint32_t clean = w & ~((~w & 0x55555555u) << 1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int f = __builtin_amdgcn_sbfe((int)clean, 2 * j, 2);
-            a[j] = __builtin_fmaf((float)f, s, a[j]);
+        for (int j = 0; j < 8; ++j) {
+            const h16x2 f = __builtin_bit_cast(h16x2, (clean << (14 - 2 * j)) & 0xC000C000u);
+            a[j] = __builtin_fmaf((float)f.x, z, a[j]);
+            a[j + 8] = __builtin_fmaf((float)f.y, z, a[j + 8]);
         }
     } else if constexpr (F == A_QSGD) {
 #pragma unroll
@@ -147,13 +154,19 @@ __device__ __forceinline__ void add_chunk(float (&a)[16], const ChunkBits<F>& c,
 }
 
 // The fast forms above rely on 0 * s being +0: for TernGrad's s and QSGD's
-// d that holds when the value is +0 or positive and finite.  Otherwise (an
-// overflowed sum of squares gives d = inf; a caller may pass anything) the
-// worker's terms are decoded one by one exactly as the decoder does.
+// d that holds when the value is +0 or positive and finite (TernGrad's also
+// on s/2 being exact, which rules out subnormal and tiny normal scales).
+// Otherwise (an overflowed sum of squares gives d = inf; a caller may pass
+// anything) the worker's terms are decoded one by one exactly as the decoder
+// does.
 template <int F>
 __device__ __forceinline__ bool needs_exact_path(float s, float z) {
     if constexpr (F == A_QSGD) return __float_as_uint(z) >= 0x7F800000u;
-    else if constexpr (F == A_TER) return __float_as_uint(s) >= 0x7F800000u;
+    else if constexpr (F == A_TER) {
+        // the fast form also needs s/2 exact: s = +0 or s >= 2^-125
+        const uint32_t b = __float_as_uint(s);
+        return b >= 0x7F800000u || b - 1u < 0x00FFFFFFu;
+    }
     else return false;
 }
 
@@ -325,6 +338,7 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
         float s, z;
         st.get(scale, zero, ng, gb, w, s, z);
         if constexpr (F == A_QSGD) z = s / 7.0f;
+        if constexpr (F == A_TER) z = s * 0.5f;
         const bool exact = needs_exact_path<F>(s, z);
         // Wave-uniform statistics arrive in scalar registers (v_readlane).
         // On gfx950 a VALU op that reads a scalar register issues at about
@@ -472,8 +486,15 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
 // nb tiles of G::B elements; tile bk belongs to statistics group
 // bk >> tshift of ng (tshift = 0 when a tile is a whole group, which
 // requantization requires).
+// TernGrad sums of whole-wave buckets with up to 2 chunks per lane fit 5
+// waves per SIMD (94 registers) when asked to; left alone the compiler
+// takes 98 and 4 waves, 3-4% slower on 64 x 2^26 in buckets of 2,048.  (Six
+// waves spill; so do 4-chunk buckets at five.)
+template <int F, class G>
+constexpr int min_waves() { return F == A_TER && G::LPB == WAVE && G::K <= 2 ? 5 : 1; }
+
 template <class G, int F, int RQBITS, bool RQ>
-__global__ void __launch_bounds__(G::THREADS)
+__global__ void __launch_bounds__(G::THREADS, (min_waves<F, G>()))
 k_dequant_acc(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
               const float* __restrict__ zero, int32_t m, int64_t n, int64_t nb, int64_t ng, int32_t tshift,
               int64_t pbytes, float* __restrict__ acc, int32_t accumulate, uint8_t* __restrict__ rq_codes,

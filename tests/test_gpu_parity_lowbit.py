@@ -357,6 +357,60 @@ def test_dequant_accumulate_arbitrary_codes_and_scales(qc, ora, fmt, group):
     assert bits_or_both_nan(acc.f32(), want), first_diff(acc.f32(), want)
 
 
+# TernGrad scales around 2^-125, the smallest scale whose half is normal
+TERN_TINY_SCALES = [
+    0x01000000,  # 2^-125
+    0x00FFFFFF,  # just below it, odd significand: its half is not exact
+    0x00FFFFFE,
+    0x00800000,  # 2^-126
+    0x00800001,
+    0x007FFFFF,  # largest subnormal
+    0x00000001,  # smallest subnormal
+    0x01000001,
+    0x01800003,
+    0x00000000,
+    0x80000000,  # -0
+    0x80800001,
+]
+TERN_WIDE_SCALES = [0x7F000001, 0x7F7FFFFF, 0x3F800001, 0x00FFFFFF, 0x7F800000, 0x7FC00000,
+                    0xFF7FFFFF, 0x00000000, 0x2F000001, 0x01000000, 0x80000001, 0x4B000001]
+
+
+@pytest.mark.parametrize("group", [64, 2048])
+def test_ternary_accumulate_scale_boundaries(qc, ora, group):
+    """TernGrad terms are summed as fma(+-2, s/2, acc) when s/2 is exact and
+    decoded one by one otherwise.  Most buckets take scales on both sides of
+    that boundary (2^-125), subnormal ones and signed zeros, over
+    accumulators of +-0 and subnormal values, so a rounded s/2 shows in the
+    sums' low bits; every fourth bucket mixes in the largest finite values,
+    infinities and NaN.  Every code value occurs (code 2 too)."""
+    m, n = len(TERN_TINY_SCALES), 9 * group + 29
+    nb = qc.nbuckets(n, group)
+    pb = qc.payload_bytes(4, n, group, 2)
+    payloads = synth.host_words(m * pb // 4, 4409 + group).view(np.uint8).copy()
+    valid = ora.payload_bytes(4, n, 2)
+    used = -(-n * 2 // 8)
+    for w in range(m):
+        payloads[w * pb + used: w * pb + valid] = 0
+    sbits = np.empty(m * nb, np.uint32)
+    for w in range(m):
+        for b in range(nb):
+            pool = TERN_WIDE_SCALES if b % 4 == 3 else TERN_TINY_SCALES
+            sbits[w * nb + b] = pool[(w + 5 * b) % len(pool)]
+    scale = sbits.view(np.float32)
+    start = synth.host_normal(n, 1e-39, seed=17)
+    start[::4] = 0.0
+    start[1::4] = -0.0
+    for accumulate in (True, False):
+        want = ora.dequant_accumulate(4, payloads, scale, None, m, n, group, 2,
+                                      acc=start if accumulate else None)
+        acc = out_f32(n)
+        acc.t.copy_(dev(start))
+        qc.qc_dequant_accumulate(4, dev(payloads), dev(scale), None, m, n, group, 2, acc.t, accumulate)
+        sync()
+        assert bits_or_both_nan(acc.f32(), want), (accumulate, first_diff(acc.f32(), want))
+
+
 def test_qsgd_accumulate_with_overflowing_norm(qc, ora):
     """Huge but finite gradients: a bucket's sum of squares overflows, the
     norm is +inf, every level is 0, and the sum must stay exact (+0 terms)."""
