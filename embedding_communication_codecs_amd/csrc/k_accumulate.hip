@@ -111,19 +111,25 @@ __device__ __forceinline__ void add_chunk(float (&a)[16], const ChunkBits<F>& c,
     } else if constexpr (F == A_TER) {
         // The term is 0 or +-s, so fma(f, s/2, a) with f in {0, 2, -2} is
         // the exact sum rounded once, as a + DQ is (z = s/2, exact for the
-        // scales this path takes).  A code whose bit 1 is cleared where its
-        // bit 0 is clear (the never-emitted code 2, like code 0, is +0) is
-        // the top two bits of an fp16 number with nothing below them:
-        // 0x0000 = +0, 0x4000 = 2, 0xC000 = -2.  One shift and one mask put
-        // codes j and j + 8 at the top of the two halves of a word, and each
-        // half feeds v_fma_mix_f32 (fp16 operand, fp32 arithmetic) directly:
-        // an fma per term and one shift or mask per two terms, against a
-        // bitfield extract, a conversion and an fma.
+        // scales this path takes).  A 2-bit code is the top two bits of an
+        // fp16 number with nothing below them: 0x0000 = +0, 0x4000 = 2,
+        // 0xC000 = -2.  One shift and one mask put codes j and j + 8 at the
+        // top of the two halves of a word, and each half feeds
+        // v_fma_mix_f32 (fp16 operand, fp32 arithmetic) directly: an fma per
+        // term and one shift or mask per two terms, against a bitfield
+        // extract, a conversion and an fma.
+        //
+        // The never-emitted code 2 decodes to +0 but reads here as 0x8000 =
+        // -0, and acc + -0 differs from acc + +0 only when acc is -0 (-0
+        // against +0).  From there on the two sums either agree bit for bit
+        // or are -0 here and +0 by the rule (a sum is -0 only as -0 + -0;
+        // every other term makes both sums equal), so a sum that ends at
+        // anything but -0 is the rule's sum, and the few that end at -0 are
+        // summed again term by term after the last worker.
         const uint32_t w = words[0];
-        const uint32_t clean = w & ~((~w & 0x55555555u) << 1);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const h16x2 f = __builtin_bit_cast(h16x2, (clean << (14 - 2 * j)) & 0xC000C000u);
+            const h16x2 f = __builtin_bit_cast(h16x2, (w << (14 - 2 * j)) & 0xC000C000u);
             a[j] = __builtin_fmaf((float)f.x, z, a[j]);
             a[j + 8] = __builtin_fmaf((float)f.y, z, a[j + 8]);
         }
@@ -187,6 +193,20 @@ __device__ __forceinline__ void add_chunk_exact(float (&a)[16], const ChunkBits<
         }
         a[j] = a[j] + t;
     }
+}
+
+// One TernGrad sum (element idx of statistics group gb), one term at a
+// time exactly as the decoder's rule gives them.
+__device__ __noinline__ float ter_sum_one(const uint8_t* __restrict__ codes, int64_t pbytes,
+                                          const float* __restrict__ scale, int64_t ng, int64_t gb, int32_t m,
+                                          int64_t idx, const float* __restrict__ acc, int32_t accumulate) {
+    float r = accumulate ? acc[idx] : 0.0f;
+    for (int32_t w = 0; w < m; ++w) {
+        const uint32_t code = (codes[(int64_t)w * pbytes + idx / 4] >> (2 * (idx % 4))) & 3u;
+        const float s = scale[(int64_t)w * ng + gb];
+        r = r + ((code & 1u) ? ((code & 2u) ? -s : s) : 0.0f);
+    }
+    return r;
 }
 
 // 2-bit uniform codes through a per-wave table in LDS.  A 2-bit code has
@@ -386,6 +406,24 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
 #pragma unroll
         for (int u = 0; u < UW - 1; ++u)
             if (w0 + u < cend) add_worker(w0 + u, slot[u]);
+    }
+
+    // TernGrad sums ending at -0 (see add_chunk): summed again term by term
+    if constexpr (F == A_TER) {
+        bool negz = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) negz |= __float_as_uint(a[k][j]) == 0x80000000u;
+        if (__any(negz)) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (__float_as_uint(a[k][j]) == 0x80000000u)
+                        a[k][j] = ter_sum_one(codes, pbytes, scale, ng, gb, m,
+                                              base + (int64_t)k * LPB * 16 + j, acc, accumulate);
+        }
     }
 
     // A lane's 16 sums are 64 contiguous bytes: full tiles of whole-wave

@@ -411,6 +411,38 @@ def test_ternary_accumulate_scale_boundaries(qc, ora, group):
         assert bits_or_both_nan(acc.f32(), want), (accumulate, first_diff(acc.f32(), want))
 
 
+@pytest.mark.parametrize("group", [64, 2048])
+@pytest.mark.parametrize("m", [1, 2, 3, 5])
+def test_ternary_accumulate_signed_zero_sums(qc, ora, group, m):
+    """Sums that stay at +-0: accumulators starting at -0 and +0, scales of
+    +0 (every code's term is +-0), -0 and a few nonzero ones, every code
+    value including the never-emitted code 2 (which decodes to +0).  Many
+    sums end at -0 or +0, and only the rule's order of signed-zero additions
+    decides which."""
+    n = 7 * group + 13
+    nb = qc.nbuckets(n, group)
+    pb = qc.payload_bytes(4, n, group, 2)
+    payloads = synth.host_words(m * pb // 4, 7100 + group + m).view(np.uint8).copy()
+    valid = ora.payload_bytes(4, n, 2)
+    used = -(-n * 2 // 8)
+    for w in range(m):
+        payloads[w * pb + used: w * pb + valid] = 0
+    pool = np.array([0x00000000] * 6 + [0x80000000, 0x3F800000], np.uint32)
+    sbits = pool[(np.arange(m * nb) * 5 + m) % pool.size]
+    scale = sbits.view(np.float32)
+    start = np.full(n, -0.0, np.float32)
+    start[::5] = 0.0
+    start[3::11] = np.float32(1.5)
+    for accumulate in (True, False):
+        want = ora.dequant_accumulate(4, payloads, scale, None, m, n, group, 2,
+                                      acc=start if accumulate else None)
+        acc = out_f32(n)
+        acc.t.copy_(dev(start))
+        qc.qc_dequant_accumulate(4, dev(payloads), dev(scale), None, m, n, group, 2, acc.t, accumulate)
+        sync()
+        assert bits_or_both_nan(acc.f32(), want), (accumulate, first_diff(acc.f32(), want))
+
+
 def test_qsgd_accumulate_with_overflowing_norm(qc, ora):
     """Huge but finite gradients: a bucket's sum of squares overflows, the
     norm is +inf, every level is 0, and the sum must stay exact (+0 terms)."""
