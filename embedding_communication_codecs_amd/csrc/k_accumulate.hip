@@ -210,41 +210,61 @@ __device__ __noinline__ float ter_sum_one(const uint8_t* __restrict__ codes, int
 }
 
 // 2-bit uniform codes through a per-wave table in LDS.  A 2-bit code has
-// four decoded values per (worker, bucket); lanes 0-3 write them (computed
-// exactly as the decoder computes them) to the wave's 256-byte-aligned
-// table, and a term becomes one v_perm (the code, times 4, as the low
-// address byte over the table's base), one ds_read_b32 and one add, where
-// the arithmetic path takes a conversion, a multiply and two adds.  The LDS
-// pipe works beside the VALU, which bounds 2-bit sums, so the codes of
-// residue r < TAB_NV (elements 4q + r of a chunk) keep the arithmetic path
-// and the rest go through the table.  Measured on the 64-worker sum of
-// 2^26 elements in buckets of 2,048: 417 us all-arithmetic (statistics in
-// scalar registers), 383 us with them in vector registers, 355 us with a
-// quarter of the terms on the VALU (TAB_NV = 1); 397 us with every term
-// through the table, 376 us with three quarters on the VALU.
-constexpr int TAB_NV = 1;
+// four decoded values per (worker, bucket), so two adjacent codes have 16;
+// per worker, lanes 0-31 write the 16 pairs (d(c0), d(c1)) of decoded
+// values, each computed exactly as the decoder computes it, to the wave's
+// 256-byte-aligned table, entry c0 + 4 c1 at byte 8 (c0 + 4 c1).  A pair of
+// terms is then one v_perm (the pair's 4 code bits, times 8, as the low
+// address byte over the table's base), one ds_read_b64 and two adds, where
+// the arithmetic path takes a conversion, a multiply and two adds per term.
+// The LDS pipe delivers 32 such terms per CU clock and works beside the
+// VALU, which bounds 2-bit sums, so 12 of a chunk's 16 terms (the pairs
+// 4q+2, 4q+3 and, for q < 2, 4q, 4q+1) go through the table and 4 (codes 8,
+// 9, 12 and 13) through the arithmetic.  Measured on the 64-worker sum of
+// 2^26 elements in buckets of 2,048 with requantization: 417 us
+// all-arithmetic (statistics in scalar registers), 383 us with them in
+// vector registers, 355 us with 12 terms through a one-code table (a v_perm
+// and a ds_read_b32 per term; 397 us with all 16).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 __device__ __forceinline__ uint32_t lds_addr(float* p) { return (uint32_t)(uintptr_t)(lds_f32*)p; }
-__device__ __forceinline__ float lds_load(uint32_t a) { return *(const lds_f32*)(uintptr_t)a; }
+__device__ __forceinline__ f32x2 lds_load2(uint32_t a) { return *(const lds_f32x2*)(uintptr_t)a; }
 __device__ __forceinline__ void lds_store(uint32_t a, float v) { *(lds_f32*)(uintptr_t)a = v; }
 
-__device__ __forceinline__ void add_chunk_u2_tab(float (&a)[16], uint32_t w, float s, float z, uint32_t tbase) {
+// lanes 0-31: float l of the pair table, d(c) for c = code (l & 1 ? 1 : 0) of entry l >> 1
+__device__ __forceinline__ void u2_pair_table_store(uint32_t tbase, float s, float z) {
+    const uint32_t l = (uint32_t)lane_id();
+    if (l < 32u) {
+        const uint32_t c = (l & 1u) ? (l >> 3) : ((l >> 1) & 3u);
+        const float p = (float)c * s;
+        lds_store(tbase + 4u * l, p + z);
+    }
+}
+
+__device__ __forceinline__ void add_chunk_u2_pairs(float (&a)[16], uint32_t w, float s, float z, uint32_t tbase) {
+    const uint32_t p01 = and_mask(w << 3, 0x78787878u);  // byte q = 8 (c(4q) + 4 c(4q+1))
+    const uint32_t p23 = and_mask(w >> 1, 0x78787878u);  // byte q = 8 (c(4q+2) + 4 c(4q+3))
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if (r < TAB_NV) {
-            const uint32_t sp = and_mask(w >> (2 * r), 0x03030303u);
+    for (int q = 0; q < 4; ++q) {
+        const f32x2 v = lds_load2(__builtin_amdgcn_perm(tbase, p23, 0x07060500u | (uint32_t)q));
+        a[4 * q + 2] = a[4 * q + 2] + v.x;
+        a[4 * q + 3] = a[4 * q + 3] + v.y;
+    }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float p = byte_f(sp, q) * s;
-                a[4 * q + r] = a[4 * q + r] + (p + z);
-            }
-        } else {
-            // byte q = 4 * code(4q + r)
-            const uint32_t sp4 = and_mask(r == 0 ? w << 2 : w >> (2 * r - 2), 0x0C0C0C0Cu);
+    for (int q = 0; q < 2; ++q) {
+        const f32x2 v = lds_load2(__builtin_amdgcn_perm(tbase, p01, 0x07060500u | (uint32_t)q));
+        a[4 * q] = a[4 * q] + v.x;
+        a[4 * q + 1] = a[4 * q + 1] + v.y;
+    }
+    const uint32_t s0 = and_mask(w, 0x03030303u);       // byte q = c(4q)
+    const uint32_t s1 = and_mask(w >> 2, 0x03030303u);  // byte q = c(4q+1)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                a[4 * q + r] = a[4 * q + r] + lds_load(__builtin_amdgcn_perm(tbase, sp4, 0x07060500u | (uint32_t)q));
-        }
+    for (int q = 2; q < 4; ++q) {
+        const float p0 = byte_f(s0, q) * s;
+        a[4 * q] = a[4 * q] + (p0 + z);
+        const float p1 = byte_f(s1, q) * s;
+        a[4 * q + 1] = a[4 * q + 1] + (p1 + z);
     }
 }
 
@@ -373,13 +393,9 @@ __device__ __forceinline__ void acc_bucket(const uint8_t* __restrict__ codes, co
                 for (int k = 0; k < K; ++k) add_chunk_exact<F>(a[k], c[k], s, z);
             }
         } else if constexpr (TAB) {
-            if (lane_id() < 4) {
-                // the decoded value of code l, rounded as the decoder rounds it
-                const float p = (float)lane_id() * s;
-                lds_store(tbase + 4u * (uint32_t)lane_id(), p + z);
-            }
+            u2_pair_table_store(tbase, s, z);
 #pragma unroll
-            for (int k = 0; k < K; ++k) add_chunk_u2_tab(a[k], c[k].v.x, s, z, tbase);
+            for (int k = 0; k < K; ++k) add_chunk_u2_pairs(a[k], c[k].v.x, s, z, tbase);
         } else {
 #pragma unroll
             for (int k = 0; k < K; ++k) add_chunk<F>(a[k], c[k], s, z);
