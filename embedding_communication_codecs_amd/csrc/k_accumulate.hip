@@ -14,10 +14,11 @@
 // The per-(worker, bucket) scale and zero are uniform across a wave when a
 // bucket spans whole waves; one vector load brings 64 workers' values into
 // a register across the wave (see Stats); each worker's pair is then
-// copied to vector registers, and 2-bit uniform terms read most of their
-// decoded values from a per-wave table in LDS.  Blocks are mapped to buckets XCD
-// by XCD (consecutive buckets on one XCD), so neighbouring buckets'
-// statistics share that XCD's L2 lines.
+// copied to vector registers.  2-bit uniform terms read most of their
+// decoded values, two at a time, from a per-wave table in LDS; a TernGrad
+// term is one fp16-operand fma.  Blocks are mapped to buckets XCD by XCD
+// (consecutive buckets on one XCD), so neighbouring buckets' statistics
+// share that XCD's L2 lines.
 //
 // Bounds: a chunk starting below n reads its codes inside the 16-byte
 // padded payload (see the payload rules in qc.h).
