@@ -440,7 +440,8 @@ __device__ __forceinline__ void qsgd_bucket(Src src, float* __restrict__ ef,
 
     float v[KH][4];
     float s[K];  // chunk k's sum of squares over the lane group: a subtree of the bucket's tree
-    float nrm = 0.0f, d = 0.0f;
+    float nrm = 0.0f, d = 0.0f, rd = 0.0f;
+    bool dok = false;
     auto sums = [&](auto k0c) {
         constexpr int C0 = decltype(k0c)::value;
 #pragma unroll
@@ -455,6 +456,8 @@ __device__ __forceinline__ void qsgd_bucket(Src src, float* __restrict__ ef,
         if constexpr (G::W > 1) ss = block_tree_sum<G::W>(ss, lds);
         nrm = sqrtf(ss);
         d = nrm / 7.0f;
+        dok = quot_divisor_ok(d);
+        if (dok) rd = 1.0f / d;
     };
     auto encode = [&](auto k0c) {
         constexpr int C0 = decltype(k0c)::value;
@@ -466,9 +469,24 @@ __device__ __forceinline__ void qsgd_bucket(Src src, float* __restrict__ ef,
             if (d != 0.0f && (FULL || i < n)) {
                 float u[4];
                 chunk_draws(elem_offset + (uint64_t)i, k0, k1, u);
+                // |v| / d through the reciprocal (quot_fast); the rare
+                // element outside its range is divided, under a wave-uniform
+                // branch so the division stays off the common path
+                float tq[4];
+                bool fast[4], all = true;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float t = fabsf(v[k][j]) / d;
+                    tq[j] = quot_fast(fabsf(v[k][j]), d, rd, dok, fast[j]);
+                    all = all && fast[j];
+                }
+                if (!__all(all)) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (!fast[j]) tq[j] = fabsf(v[k][j]) / d;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = tq[j];
                     const float fl = floorf(t);
                     const float frac = t - fl;
                     uint32_t level = (uint32_t)fl + (u[j] < frac ? 1u : 0u);

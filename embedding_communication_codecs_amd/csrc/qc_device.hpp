@@ -248,6 +248,29 @@ __device__ __forceinline__ void store_wave_span16(float* __restrict__ dst, const
 }
 
 // --------------------------------------------------------------- misc
+// ------------------------------------------------------- division by d
+// fl(x / d) without a division, for x >= +0 and a divisor shared by many
+// x: with r = fl(1/d), q0 = fl(x r) is within an ulp of x/d, the
+// remainder x - q0 d is exact (one fma), and fl(q0 + rem r) is the
+// correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990), as
+// long as nothing underflows or overflows: d and 1/d normal (the caller's
+// `dok`), x finite and >= 2^-102 (so the remainder does not fall below the
+// subnormal grid) and the quotient in [2^-100, 2^126].  x = +0 gives +0.
+// Otherwise `fast` is false and the caller divides.
+__device__ __forceinline__ float quot_fast(float x, float d, float r, bool dok, bool& fast) {
+    const float q0 = x * r;
+    const float rem = __builtin_fmaf(-q0, d, x);
+    const float aq = fabsf(q0);
+    fast = dok && (x == 0.0f || (x >= 0x1p-102f && x <= 0x1.fffffep127f && aq >= 0x1p-100f && aq <= 0x1p126f));
+    return __builtin_fmaf(rem, r, q0);
+}
+
+// d and 1/d both normal
+__device__ __forceinline__ bool quot_divisor_ok(float d) {
+    const float a = fabsf(d);
+    return a >= 0x1p-126f && a <= 0x1p126f;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 }  // namespace qc

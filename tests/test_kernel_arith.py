@@ -1,4 +1,4 @@
-"""Host checks of two arithmetic shortcuts the GPU kernels take, each
+"""Host checks of arithmetic shortcuts the GPU kernels take, each
 claimed to give exactly the result of the plain formula:
 
 * the QSGD decoder's step size d = fl(norm / 7) computed without a
@@ -6,6 +6,9 @@ claimed to give exactly the result of the plain formula:
   exact remainder (checked here over every fp32 bit pattern);
 * the rowwise FP8 encoder's row scale fl(amax / 448), computed the same
   way for amax >= 2^-120 (checked over every such fp32 value);
+* the QSGD encoder's ratio fl(|v| / d), d shared by the bucket, computed
+  from r = fl(1/d) the same way inside the guard it states (checked over
+  billions of pairs, densest where the ratio decides a level);
 * the rowwise FP8 encoder's E4M3 code of fl(x / scale), computed from
   fl(x * r) with r within an ulp of 1/scale, except where that product lies
   within 8 ulps of an E4M3 rounding point or below 2^-6 (checked here on
@@ -80,6 +83,79 @@ int main(void) {
 """
 
 
+# fl(x / d) for x >= +0 and a divisor shared by a bucket (quot_fast in the
+# kernels' device header): q0 = fl(x r), r = fl(1/d), then
+# fl(q0 + fl(x - q0 d) r) with fmas, taken only when d and 1/d are normal,
+# x is +0 or finite and at least 2^-102, and 2^-100 <= |q0| <= 2^126; else
+# the kernel divides.  Checked
+# here against x / d over a spread of divisors (significands at both ends
+# of the binade, random ones, exponents at both limits of the guard) and,
+# per divisor of either sign, every float x whose quotient is about 1 to 8
+# (where QSGD's |v|/d decides a level above 0), every 16th one down to
+# quotients of 2^-4, every 256th down to 2^-40, and every 4093rd over the
+# rest of the range, x below 2^-102 included.
+QUOT_C = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+static float f(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+static uint32_t b(float x) { uint32_t v; memcpy(&v, &x, 4); return v; }
+static int dok(float d) { const float a = fabsf(d); return a >= 0x1p-126f && a <= 0x1p126f; }
+static float quot(float x, float d, float r, int ok, int* fast) {
+    const float q0 = x * r;
+    const float rem = fmaf(-q0, d, x);
+    const float aq = fabsf(q0);
+    *fast = ok && (x == 0.0f || (x >= 0x1p-102f && x <= 0x1.fffffep127f && aq >= 0x1p-100f && aq <= 0x1p126f));
+    return fmaf(rem, r, q0);
+}
+int main(void) {
+    uint32_t ds[200];
+    int nd = 0;
+    uint64_t st = 0x9E3779B97F4A7C15ull;
+    for (uint32_t m = 0; m < 24; ++m) ds[nd++] = 0x3F800000u + m;             /* 1 + small */
+    for (uint32_t m = 0; m < 24; ++m) ds[nd++] = 0x3FFFFFFFu - m;             /* 2 - small */
+    ds[nd++] = 0x00800000u; ds[nd++] = 0x00800001u; ds[nd++] = 0x00FFFFFFu;   /* 2^-126 .. */
+    ds[nd++] = 0x7E800000u; ds[nd++] = 0x7E7FFFFFu; ds[nd++] = 0x7E800001u;   /* 2^126 .. */
+    ds[nd++] = 0x3EDB6DB7u;                                                   /* ~ 3/7 */
+    while (nd < 200) {
+        st ^= st << 13; st ^= st >> 7; st ^= st << 17;
+        ds[nd++] = 0x00800000u + (uint32_t)(st % (0x7F000000u - 0x00800000u));
+    }
+    unsigned long long bad = 0, fastn = 0;
+    for (int t = 0; t < nd; ++t) {
+        const float d = f(ds[t]);
+        const int ok = dok(d);
+        const float r = ok ? 1.0f / d : 0.0f;
+        const long long ed = (ds[t] >> 23) & 0xFF;
+        #pragma omp parallel for reduction(+:bad,fastn) schedule(dynamic)
+        for (long long e = 0; e < 255; ++e) {
+            const long long rel = e - ed;  /* quotient's binade, about */
+            uint32_t step = 4093u;
+            if (rel >= 0 && rel <= 3) step = 1u;
+            else if (rel >= -4 && rel <= 3) step = 16u;
+            else if (rel >= -40 && rel <= 3) step = 256u;
+            for (uint32_t m = 0; m < (1u << 23); m += step) {
+                for (int sg = 0; sg < 2; ++sg) {  /* d of either sign; x >= +0 */
+                    const float x = f(((uint32_t)e << 23) | m);
+                    const float dd = sg ? -d : d, rr = sg ? -r : r;
+                    int fast;
+                    const float got = quot(x, dd, rr, ok, &fast);
+                    if (!fast) continue;
+                    ++fastn;
+                    const float want = x / dd;
+                    if (b(got) != b(want)) ++bad;
+                }
+            }
+        }
+    }
+    printf("%llu\n", bad);
+    fprintf(stderr, "%llu\n", fastn);
+    return 0;
+}
+"""
+
+
 def run_c(src_text):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
@@ -103,6 +179,13 @@ def test_div448_every_float():
     rounded amax/448 wherever the kernel uses it (amax in [2^-120, max])."""
     assert np.float32(1.0) / np.float32(448.0) == np.float32(float.fromhex("0x1.24924ap-9"))
     assert run_c(DIV448_C) == 0
+
+
+@pytest.mark.slow
+def test_shared_divisor_quotient_matches_division():
+    """The corrected reciprocal product equals x / d bit for bit wherever
+    the kernels' guard takes it."""
+    assert run_c(QUOT_C) == 0
 
 
 @pytest.mark.slow
