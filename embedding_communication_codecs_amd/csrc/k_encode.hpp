@@ -469,21 +469,10 @@ __device__ __forceinline__ void qsgd_bucket(Src src, float* __restrict__ ef,
             if (d != 0.0f && (FULL || i < n)) {
                 float u[4];
                 chunk_draws(elem_offset + (uint64_t)i, k0, k1, u);
-                // |v| / d through the reciprocal (quot_fast); the rare
-                // element outside its range is divided, under a wave-uniform
-                // branch so the division stays off the common path
+                // |v| / d through the bucket's reciprocal (quot_n)
+                const float ax[4] = {fabsf(v[k][0]), fabsf(v[k][1]), fabsf(v[k][2]), fabsf(v[k][3])};
                 float tq[4];
-                bool fast[4], all = true;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    tq[j] = quot_fast(fabsf(v[k][j]), d, rd, dok, fast[j]);
-                    all = all && fast[j];
-                }
-                if (!__all(all)) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (!fast[j]) tq[j] = fabsf(v[k][j]) / d;
-                }
+                quot_n<4>(ax, d, rd, dok, tq);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float t = tq[j];

@@ -255,14 +255,33 @@ __device__ __forceinline__ void store_wave_span16(float* __restrict__ dst, const
 // correctly rounded quotient (Markstein, IBM J. Res. Dev. 34(1), 1990), as
 // long as nothing underflows or overflows: d and 1/d normal (the caller's
 // `dok`), x finite and >= 2^-102 (so the remainder does not fall below the
-// subnormal grid) and the quotient in [2^-100, 2^126].  x = +0 gives +0.
-// Otherwise `fast` is false and the caller divides.
+// subnormal grid) and the quotient in [2^-100, 2^126].  x = +0 gives +0
+// (and x = -0 gives +0 too, where x / d is -0).  Otherwise `fast` is false
+// and the caller divides.
 __device__ __forceinline__ float quot_fast(float x, float d, float r, bool dok, bool& fast) {
     const float q0 = x * r;
     const float rem = __builtin_fmaf(-q0, d, x);
     const float aq = fabsf(q0);
     fast = dok && (x == 0.0f || (x >= 0x1p-102f && x <= 0x1.fffffep127f && aq >= 0x1p-100f && aq <= 0x1p126f));
     return __builtin_fmaf(rem, r, q0);
+}
+
+// q[j] = fl(x[j] / d) for N values x >= +0 or NaN (a -0 gives +0), r = fl(1/d):
+// quot_fast, and the division for the rare value outside its range, under
+// a wave-uniform branch so the division stays off the common path.
+template <int N>
+__device__ __forceinline__ void quot_n(const float (&x)[N], float d, float r, bool dok, float (&q)[N]) {
+    bool fast[N], all = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        q[j] = quot_fast(x[j], d, r, dok, fast[j]);
+        all = all && fast[j];
+    }
+    if (!__all(all)) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            if (!fast[j]) q[j] = x[j] / d;
+    }
 }
 
 // d and 1/d both normal
