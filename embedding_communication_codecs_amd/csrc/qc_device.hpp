@@ -247,7 +247,6 @@ __device__ __forceinline__ void store_wave_span16(float* __restrict__ dst, const
     span16_store(dst, xw);
 }
 
-// --------------------------------------------------------------- misc
 // ------------------------------------------------------- division by d
 // fl(x / d) without a division, for x >= +0 and a divisor shared by many
 // x: with r = fl(1/d), q0 = fl(x r) is within an ulp of x/d, the
@@ -290,6 +289,7 @@ __device__ __forceinline__ bool quot_divisor_ok(float d) {
     return a >= 0x1p-126f && a <= 0x1p126f;
 }
 
+// --------------------------------------------------------------- misc
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 }  // namespace qc
