@@ -376,7 +376,7 @@ TERN_WIDE_SCALES = [0x7F000001, 0x7F7FFFFF, 0x3F800001, 0x00FFFFFF, 0x7F800000, 
                     0xFF7FFFFF, 0x00000000, 0x2F000001, 0x01000000, 0x80000001, 0x4B000001]
 
 
-@pytest.mark.parametrize("group", [64, 2048])
+@pytest.mark.parametrize("group", [64, 2048, 8192, 65536])
 def test_ternary_accumulate_scale_boundaries(qc, ora, group):
     """TernGrad terms are summed as fma(+-2, s/2, acc) when s/2 is exact and
     decoded one by one otherwise.  Most buckets take scales on both sides of
@@ -411,7 +411,7 @@ def test_ternary_accumulate_scale_boundaries(qc, ora, group):
         assert bits_or_both_nan(acc.f32(), want), (accumulate, first_diff(acc.f32(), want))
 
 
-@pytest.mark.parametrize("group", [64, 2048])
+@pytest.mark.parametrize("group", [64, 512, 2048, 4096, 8192, 65536])
 @pytest.mark.parametrize("m", [1, 2, 3, 5])
 def test_ternary_accumulate_signed_zero_sums(qc, ora, group, m):
     """Sums that stay at +-0: accumulators starting at -0 and +0, scales of
