@@ -91,17 +91,22 @@ def test_uniform_quotient_edges(qc, ora, bits, stochastic):
     assert bits_equal(ef_d.f32(), ef_h), first_diff(ef_d.f32(), ef_h)
 
 
-def test_qsgd_quotient_edges(qc, ora):
+@pytest.mark.parametrize("bucket", [64, 512, 4096, 65536])
+def test_qsgd_quotient_edges(qc, ora, bucket):
+    # the 64-element rows tiled over larger buckets (a ragged last one),
+    # without the row whose squares overflow (it would make every norm inf)
     x = rows_general()
+    if bucket > B:
+        x = np.resize(np.concatenate([x[:B], x[2 * B:]]), 2 * bucket + 37)
     n = x.size
     for step, seed in enumerate((7, 8)):
         ef_h = synth.host_normal(n, 1e-31, seed=30 + step)
         ef_d = dev_ef(ef_h)
-        words = Out(qc.payload_bytes(qc.QC_QSGD, n, B, 16))
-        norm = out_f32(qc.nbuckets(n, B))
-        qc.qc_encode_qsgd(dev(x), ef_d.t, n, B, 16, seed, 0, words.t, norm.t)
+        words = Out(qc.payload_bytes(qc.QC_QSGD, n, bucket, 16))
+        norm = out_f32(qc.nbuckets(n, bucket))
+        qc.qc_encode_qsgd(dev(x), ef_d.t, n, bucket, 16, seed, 0, words.t, norm.t)
         sync()
-        p, nr = ora.encode_qsgd(x, ef_h, B, seed, 0)
+        p, nr = ora.encode_qsgd(x, ef_h, bucket, seed, 0)
         assert bits_equal(words.host(), p), first_diff(words.host(), p)
         assert bits_equal(norm.f32(), nr) and bits_equal(ef_d.f32(), ef_h)
 
